@@ -1,0 +1,251 @@
+/*
+ * oracle.c — CPU oracle for the NVFP4 weight-only projection  y = x · dequant(W)^T.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or call
+ * this file; only the tests, the smoke check and the benchmark's CPU-baseline
+ * leg do.  It shares no code, header, table or helper with the HIP library.
+ *
+ * What it computes (plain definition, fp64 throughout):
+ *
+ *     W[n,k] = e2m1(code[n,k]) * e4m3(scale[n, floor(k/16)]) * g
+ *     y[m,n] = sum_k  bf16(x[m,k]) * W[n,k]
+ *     S[m,n] = sum_k |bf16(x[m,k]) * W[n,k]|        (tolerance base)
+ *
+ * Sources.  The weight format is the NVFP4 checkpoint format named on the
+ * FlashRT "Qwen3.6 NVFP4 usage" page (constructor argument table: a
+ * compressed-tensors "nvfp4-pack-quantized" checkpoint) and on the Qwen3x-Orin
+ * README (repository map: FP8 and NVFP4 format primitives).  Neither page gives
+ * bit layouts, so:
+ *   - e2m1 follows the OCP Microscaling Formats (MX) v1.0 spec, FP4 E2M1
+ *     element: 1 sign, 2 exponent (bias 1), 1 mantissa bit, E=0 subnormal,
+ *     no Inf/NaN;
+ *   - e4m3 follows the OCP 8-bit Floating Point spec, E4M3 ("fn"): bias 7,
+ *     subnormals m/8 * 2^-6, S.1111.111 = NaN, no Inf (not the FNUZ variant);
+ *   - codes are packed two per byte, element 2j in the low nibble (bits 3:0),
+ *     element 2j+1 in the high nibble;
+ *   - canonical layouts: codes u8 [N][K/2], scales u8 [N][K/16], x bf16 bits
+ *     [M][K] row-major, y [M][N];
+ *   - the fp32 global scale g multiplies.
+ * Row dequantisation into an fp64 buffer is exact: q*s has at most 6
+ * significant bits and g 24, so q*s*g fits in 53 bits.
+ *
+ * Parity pins (see tests/): the e2m1 table against the OCP table fixture, all
+ * 256 e4m3 encodings against torch.float8_e4m3fn, bf16 against torch.bfloat16,
+ * and the projection against exact rational arithmetic on tiny inputs.
+ */
+#include <math.h>
+#include <pthread.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ---- element formats (closed forms) ----------------------------------- */
+
+/* e2m1 code (low 4 bits of c) -> value.  OCP MX v1.0 FP4 E2M1. */
+double orc_e2m1(unsigned c)
+{
+    unsigned sign = (c >> 3) & 1u;
+    unsigned e = (c >> 1) & 3u;
+    unsigned m = c & 1u;
+    double mag;
+    if (e == 0)
+        mag = 0.5 * (double)m;                       /* subnormal: m/2 * 2^(1-1) */
+    else
+        mag = ldexp(1.0 + 0.5 * (double)m, (int)e - 1); /* 2^(e-1) * (1 + m/2) */
+    return sign ? -mag : mag;
+}
+
+/* e4m3 byte -> value.  OCP OFP8 E4M3 ("fn"): bias 7, NaN = S.1111.111. */
+double orc_e4m3(unsigned b)
+{
+    unsigned sign = (b >> 7) & 1u;
+    unsigned e = (b >> 3) & 15u;
+    unsigned m = b & 7u;
+    double mag;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        mag = ldexp((double)m, -9);                  /* m/8 * 2^-6 */
+    else
+        mag = ldexp(1.0 + (double)m / 8.0, (int)e - 7);
+    return sign ? -mag : mag;
+}
+
+/* bf16 bit pattern -> value: the upper half of an IEEE binary32. */
+double orc_bf16(uint16_t bits)
+{
+    uint32_t u = (uint32_t)bits << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* ---- one weight row ----------------------------------------------------- */
+
+/* w[k] = e2m1(code[n,k]) * e4m3(scale[n,k/16]) * g for one row n, k in [0,K). */
+void orc_dequant_row(const uint8_t *codes_row, const uint8_t *scales_row,
+                     int64_t K, double g, double *w)
+{
+    for (int64_t k = 0; k < K; ++k) {
+        uint8_t byte = codes_row[k / 2];
+        unsigned code = (k % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4);
+        double s = orc_e4m3(scales_row[k / 16]);
+        w[k] = orc_e2m1(code) * s * g;
+    }
+}
+
+/* ---- the projection ----------------------------------------------------- */
+
+typedef struct {
+    int64_t M, N, K;
+    const uint8_t *codes, *scales;
+    double g;
+    const uint16_t *x;
+    const int64_t *rows;   /* NULL: all rows; else row indices to evaluate */
+    int64_t nrows;
+    double *y, *S;         /* [M][nrows] */
+    int64_t r0, r1;        /* this worker's slice of [0,nrows) */
+    int status;
+} orc_job;
+
+static void *orc_worker(void *arg)
+{
+    orc_job *j = (orc_job *)arg;
+    double *w = (double *)malloc((size_t)j->K * sizeof(double));
+    double *xd = (double *)malloc((size_t)(j->M * j->K) * sizeof(double));
+    if (!w || !xd) {
+        free(w);
+        free(xd);
+        j->status = -1;
+        return NULL;
+    }
+    for (int64_t i = 0; i < j->M * j->K; ++i)
+        xd[i] = orc_bf16(j->x[i]);
+    for (int64_t r = j->r0; r < j->r1; ++r) {
+        int64_t n = j->rows ? j->rows[r] : r;
+        orc_dequant_row(j->codes + n * (j->K / 2), j->scales + n * (j->K / 16),
+                        j->K, j->g, w);
+        for (int64_t m = 0; m < j->M; ++m) {
+            const double *xm = xd + m * j->K;
+            double acc = 0.0, absacc = 0.0;
+            for (int64_t k = 0; k < j->K; ++k) {
+                double t = xm[k] * w[k];
+                acc += t;
+                absacc += fabs(t);
+            }
+            j->y[m * j->nrows + r] = acc;
+            j->S[m * j->nrows + r] = absacc;
+        }
+    }
+    free(w);
+    free(xd);
+    j->status = 0;
+    return NULL;
+}
+
+/*
+ * y[m][r], S[m][r] for the weight rows listed in rows[0..nrows) (rows == NULL:
+ * every row, nrows must equal N).  Work is split over rows on nthreads POSIX
+ * threads.  Returns 0, or -1 on a bad argument or allocation failure.
+ */
+int orc_proj_rows(int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+                  const uint8_t *scales, double g, const uint16_t *x,
+                  const int64_t *rows, int64_t nrows, double *y, double *S,
+                  int nthreads)
+{
+    if (M < 0 || N < 0 || K < 0 || K % 16 != 0 || nrows < 0)
+        return -1;
+    if (!rows && nrows != N)
+        return -1;
+    if (rows)
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= N)
+                return -1;
+    if (nthreads < 1)
+        nthreads = 1;
+    if (nrows == 0 || M == 0)
+        return 0;
+    if (nthreads > nrows)
+        nthreads = (int)nrows;
+    orc_job *jobs = (orc_job *)calloc((size_t)nthreads, sizeof(orc_job));
+    pthread_t *tid = (pthread_t *)calloc((size_t)nthreads, sizeof(pthread_t));
+    if (!jobs || !tid) {
+        free(jobs);
+        free(tid);
+        return -1;
+    }
+    int rc = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        orc_job *j = &jobs[t];
+        j->M = M; j->N = N; j->K = K;
+        j->codes = codes; j->scales = scales; j->g = g; j->x = x;
+        j->rows = rows; j->nrows = nrows; j->y = y; j->S = S;
+        j->r0 = nrows * t / nthreads;
+        j->r1 = nrows * (t + 1) / nthreads;
+        j->status = -1;
+        if (pthread_create(&tid[t], NULL, orc_worker, j) != 0) {
+            orc_worker(j);   /* run inline if a thread cannot start */
+            tid[t] = 0;
+        }
+    }
+    for (int t = 0; t < nthreads; ++t) {
+        if (tid[t])
+            pthread_join(tid[t], NULL);
+        if (jobs[t].status != 0)
+            rc = -1;
+    }
+    free(jobs);
+    free(tid);
+    return rc;
+}
+
+/* Full projection: y[M][N], S[M][N]. */
+int orc_proj(int64_t M, int64_t N, int64_t K, const uint8_t *codes,
+             const uint8_t *scales, double g, const uint16_t *x, double *y,
+             double *S, int nthreads)
+{
+    return orc_proj_rows(M, N, K, codes, scales, g, x, NULL, N, y, S, nthreads);
+}
+
+/* ---- the acceptance test ------------------------------------------------ */
+
+/*
+ * Element test against the projection's stated tolerance:
+ *     |y_gpu - y_ref| <= rtol * S      (S = sum_k |x_k * w_k|, fp64)
+ * with the special cases: S == 0 requires y_gpu == 0 exactly; a NaN y_ref
+ * requires a NaN y_gpu; a finite y_ref requires a finite y_gpu.
+ * Returns the number of failing elements; *max_ratio receives the largest
+ * |y_gpu - y_ref| / S over elements with S > 0 (diagnostic).
+ */
+int64_t orc_check(int64_t count, const double *yref, const double *S,
+                  const float *ygpu, double rtol, double *max_ratio)
+{
+    int64_t bad = 0;
+    double worst = 0.0;
+    for (int64_t i = 0; i < count; ++i) {
+        double r = yref[i], s = S[i], v = (double)ygpu[i];
+        if (isnan(r)) {
+            if (!isnan(v))
+                ++bad;
+            continue;
+        }
+        if (!isfinite(v)) {
+            ++bad;
+            continue;
+        }
+        double d = fabs(v - r);
+        if (s == 0.0) {
+            if (v != 0.0)
+                ++bad;
+            continue;
+        }
+        double q = d / s;
+        if (q > worst)
+            worst = q;
+        if (d > rtol * s)
+            ++bad;
+    }
+    if (max_ratio)
+        *max_ratio = worst;
+    return bad;
+}

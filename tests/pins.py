@@ -1,0 +1,311 @@
+"""Pins of the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function takes a loaded oracle library (``oracle.load(path)``)
+and raises ``AssertionError`` when the oracle disagrees with:
+
+* the OCP e2m1 and e4m3 tables (``tests/golden``),
+* ``torch.float8_e4m3fn`` and ``torch.bfloat16`` decoding (library routines),
+* exact integer arithmetic on tiny dyadic inputs (brute force),
+* closed-form special cases (one-hot activations) and invariants.
+
+The pins never call the oracle's own decoders to build expected values, so a
+plausible mistake in the oracle (a swapped nibble, a wrong exponent bias, a
+dropped term, a transposed operand) fails at least one of them —
+``test_oracle_mutants.py`` plants such mistakes and checks exactly that.
+"""
+from __future__ import annotations
+
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+# ---- independent decoders -------------------------------------------------
+
+def golden_e2m1():
+    """code -> value from the OCP MX fixture."""
+    table = {}
+    with open(os.path.join(GOLDEN, "e2m1_ocp_mx_v1.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            parts = line.split()
+            table[int(parts[0], 16)] = float(parts[-1])
+    assert sorted(table) == list(range(16))
+    return table
+
+
+def golden_e4m3_landmarks():
+    out = {}
+    with open(os.path.join(GOLDEN, "e4m3_ocp_ofp8_landmarks.txt")) as f:
+        for line in f:
+            line = line.strip()
+            if not line or line.startswith("#"):
+                continue
+            b, v = line.split()
+            out[int(b, 16)] = float(v)
+    return out
+
+
+def torch_e4m3_table() -> np.ndarray:
+    """All 256 e4m3 encodings decoded by torch.float8_e4m3fn (fp64)."""
+    return torch.arange(256, dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def torch_bf16(bits: np.ndarray) -> np.ndarray:
+    t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
+    return t.view(torch.bfloat16).to(torch.float64).numpy()
+
+
+def independent_dequant(codes: np.ndarray, scales: np.ndarray, g: float) -> np.ndarray:
+    """W[N][K] in fp64 from the golden e2m1 table and torch's e4m3 decode."""
+    e2 = np.array([golden_e2m1()[c] for c in range(16)], dtype=np.float64)
+    e4 = torch_e4m3_table()
+    N = codes.shape[0]
+    K = codes.shape[1] * 2
+    q = np.empty((N, K), dtype=np.float64)
+    q[:, 0::2] = e2[codes & 0x0F]
+    q[:, 1::2] = e2[codes >> 4]
+    s = np.repeat(e4[scales], 16, axis=1)
+    return q * s * np.float64(g)
+
+
+# ---- tiny dyadic inputs for the exact check ---------------------------------
+
+def tiny_inputs(M, N, K, seed, x_floor=2.0 ** -20, nan_free=True):
+    """Random codes over all 16, random finite e4m3 scales, bf16 N(0,1) x with
+    |x| < 2^3 and every |x| < x_floor set to 0."""
+    rng = np.random.default_rng(seed)
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(N, K // 16), dtype=np.uint8)
+    if nan_free:
+        scales[(scales & 0x7F) == 0x7F] = 0x7E
+    xf = rng.standard_normal((M, K))
+    xf = np.clip(xf, -7.9, 7.9)
+    xbits = torch.from_numpy(xf).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    xv = torch_bf16(xbits)
+    xbits = np.where(np.abs(xv) < x_floor, np.uint16(0), xbits).astype(np.uint16)
+    return codes, scales, xbits
+
+
+def exact_projection(codes, scales, g, xbits):
+    """Exact y as Python Fractions, by integer arithmetic.
+
+    x has 8 significant bits and |x| >= 2^-20 (or 0), so x * 2^27 is an integer;
+    q*s is a multiple of 2^-10, so q*s * 2^10 is an integer; every product is an
+    integer multiple of 2^-37 below 2^52 and a K <= 256 sum stays below 2^61.
+    """
+    xv = torch_bf16(xbits)
+    xi = np.rint(xv * 2.0 ** 27).astype(np.int64)
+    assert np.array_equal(xi.astype(np.float64) * 2.0 ** -27, xv), "x not on the 2^-27 grid"
+    w = independent_dequant(codes, scales, 1.0)
+    wi = np.rint(w * 2.0 ** 10).astype(np.int64)
+    assert np.array_equal(wi.astype(np.float64) * 2.0 ** -10, w)
+    K = xbits.shape[1]
+    assert K <= 256
+    yi = xi @ wi.T                                  # exact in int64 (< 2^61)
+    gf = Fraction(g)
+    return [[Fraction(int(v), 2 ** 37) * gf for v in row] for row in yi]
+
+
+# ---- pins -----------------------------------------------------------------
+
+def pin_e2m1_table(lib):
+    table = golden_e2m1()
+    for c in range(16):
+        v = oracle.e2m1(c, lib)
+        assert v == table[c] and math.copysign(1, v) == math.copysign(1, table[c]), (c, v)
+
+
+def pin_e4m3_torch(lib):
+    ref = torch_e4m3_table()
+    for b in range(256):
+        v = oracle.e4m3(b, lib)
+        if math.isnan(ref[b]):
+            assert math.isnan(v), (b, v)
+        else:
+            assert v == ref[b] and math.copysign(1, v) == math.copysign(1, ref[b]), (b, v, ref[b])
+
+
+def pin_e4m3_landmarks(lib):
+    for b, want in golden_e4m3_landmarks().items():
+        v = oracle.e4m3(b, lib)
+        if math.isnan(want):
+            assert math.isnan(v), (b, v)
+        else:
+            assert v == want and math.copysign(1, v) == math.copysign(1, want), (b, v, want)
+
+
+def pin_bf16_torch(lib):
+    rng = np.random.default_rng(7)
+    bits = np.concatenate([rng.integers(0, 65536, 4000, dtype=np.uint16),
+                           np.array([0x0000, 0x8000, 0x3F80, 0xBF80, 0x7F7F, 0x0001, 0x7F80],
+                                    dtype=np.uint16)])
+    ref = torch_bf16(bits)
+    for b, r in zip(bits, ref):
+        v = oracle.bf16(int(b), lib)
+        if math.isnan(r):
+            assert math.isnan(v)
+        else:
+            assert v == r, (hex(int(b)), v, r)
+
+
+def pin_dequant_rows(lib):
+    """Row dequantisation equals the independently decoded W, bit for bit."""
+    rng = np.random.default_rng(11)
+    N, K = 9, 96
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 256, size=(N, K // 16), dtype=np.uint8)
+    for g in (1.0, 2.0 ** -10, float(np.float32(4.4531e-05))):
+        W = independent_dequant(codes, scales, g)
+        for n in range(N):
+            w = oracle.dequant_row(codes[n], scales[n], K, g, lib)
+            same = (w == W[n]) | (np.isnan(w) & np.isnan(W[n]))
+            assert same.all(), (n, g, np.nonzero(~same))
+
+
+SHAPES_T4 = [(M, N, K) for M in (1, 2, 7, 16, 33) for N in (1, 16, 17, 64)
+             for K in (16, 32, 48, 256)]
+
+
+def pin_exact_tiny(lib, shapes=None, seed0=100):
+    """fp64 projection on tiny dyadic inputs.
+
+    Strict inputs (|x| >= 2^-8, power-of-two g): every partial sum has at most
+    48 significant bits, so the fp64 oracle must equal the exact value bit for
+    bit.  General inputs (|x| >= 2^-20, any fp32 g): within the fp64
+    summation bound K * 2^-53 * S of the correctly rounded exact value.
+    """
+    shapes = shapes or SHAPES_T4
+    for i, (M, N, K) in enumerate(shapes):
+        for strict in (True, False):
+            codes, scales, xb = tiny_inputs(M, N, K, seed0 + 2 * i + strict,
+                                            x_floor=2.0 ** -8 if strict else 2.0 ** -20)
+            for g in ((1.0, 2.0 ** -10) if strict else (float(np.float32(3.3e-5)),)):
+                y, S = oracle.proj(codes, scales, g, xb, nthreads=2, lib=lib)
+                ex = exact_projection(codes, scales, g, xb)
+                for m in range(M):
+                    for n in range(N):
+                        e = float(ex[m][n])
+                        if strict:
+                            assert y[m, n] == e, (M, N, K, m, n, y[m, n], e)
+                        else:
+                            assert abs(y[m, n] - e) <= K * 2.0 ** -53 * S[m, n] + 1e-300, \
+                                (M, N, K, m, n, y[m, n], e)
+
+
+def pin_exact_tiny_fast(lib):
+    pin_exact_tiny(lib, [(1, 17, 48), (7, 16, 256), (33, 5, 32), (2, 64, 16)], seed0=900)
+
+
+def pin_abs_sum(lib):
+    """S equals sum |x * w| computed independently (fp64, same order of terms
+    does not matter at this size: all terms are exact and non-negative)."""
+    codes, scales, xb = tiny_inputs(3, 8, 64, 5)
+    W = independent_dequant(codes, scales, 0.5)
+    X = torch_bf16(xb)
+    y, S = oracle.proj(codes, scales, 0.5, xb, lib=lib)
+    S_ref = np.abs(X) @ np.abs(W).T
+    assert np.allclose(S, S_ref, rtol=1e-14, atol=0), (S, S_ref)
+    assert (S >= np.abs(y)).all()
+
+
+def pin_one_hot(lib):
+    """x = e_k returns exactly the dequantised column W[:, k] (closed form)."""
+    rng = np.random.default_rng(3)
+    N, K = 24, 64
+    codes = rng.integers(0, 256, size=(N, K // 2), dtype=np.uint8)
+    scales = rng.integers(0, 0x7F, size=(N, K // 16), dtype=np.uint8)
+    g = float(np.float32(0.37))
+    W = independent_dequant(codes, scales, g)
+    one = 0x3F80                                   # bf16 bits of 1.0
+    x = np.zeros((K, K), dtype=np.uint16)
+    x[np.arange(K), np.arange(K)] = one
+    y, S = oracle.proj(codes, scales, g, x, lib=lib)
+    assert np.array_equal(y, W.T), "one-hot rows do not return the dequantised columns"
+    assert np.array_equal(S, np.abs(W.T))
+
+
+def pin_invariants(lib):
+    codes, scales, xb = tiny_inputs(5, 12, 80, 21)
+    g = 0.75
+    y, S = oracle.proj(codes, scales, g, xb, lib=lib)
+    # y(-x) = -y(x): flip the bf16 sign bit
+    yn, _ = oracle.proj(codes, scales, g, xb ^ np.uint16(0x8000), lib=lib)
+    assert np.array_equal(yn, -y)
+    # g -> 2g doubles y exactly
+    y2, _ = oracle.proj(codes, scales, 2 * g, xb, lib=lib)
+    assert np.array_equal(y2, 2 * y)
+    # permuting W's rows permutes y's columns
+    perm = np.random.default_rng(1).permutation(codes.shape[0])
+    yp, _ = oracle.proj(codes[perm], scales[perm], g, xb, lib=lib)
+    assert np.array_equal(yp, y[:, perm])
+    # x = 0 gives y = 0 and S = 0
+    y0, S0 = oracle.proj(codes, scales, g, np.zeros_like(xb), lib=lib)
+    assert not y0.any() and not S0.any()
+    # a zero scale block contributes nothing: same as zeroing its codes
+    sc = scales.copy()
+    sc[3, 2] = 0
+    cz = codes.copy()
+    cz[3, 2 * 8:3 * 8] = 0
+    ya, _ = oracle.proj(codes, sc, g, xb, lib=lib)
+    yb, _ = oracle.proj(cz, scales, g, xb, lib=lib)
+    assert np.array_equal(ya[:, 3], yb[:, 3])
+    # every output only depends on its own row: evaluating a row subset agrees
+    rows = np.array([7, 0, 11, 7])
+    yr, Sr = oracle.proj_rows(codes, scales, g, xb, rows, lib=lib)
+    assert np.array_equal(yr, y[:, rows]) and np.array_equal(Sr, S[:, rows])
+
+
+def pin_nan_scale(lib):
+    """A NaN scale makes its row's outputs NaN (NaN * anything), others stay finite."""
+    codes, scales, xb = tiny_inputs(3, 6, 48, 8)
+    scales[2, 1] = 0x7F
+    scales[4, 0] = 0xFF
+    y, S = oracle.proj(codes, scales, 1.0, xb, lib=lib)
+    assert np.isnan(y[:, 2]).all() and np.isnan(y[:, 4]).all()
+    assert np.isfinite(np.delete(y, [2, 4], axis=1)).all()
+
+
+def pin_check(lib):
+    """The acceptance test's semantics."""
+    yref = np.array([1.0, 0.0, np.nan, 5.0, -2.0, 0.0])
+    S = np.array([10.0, 0.0, 1.0, 1.0, 1.0, 3.0])
+    ok = np.array([1.0 + 0.0199, 0.0, np.nan, 5.0 - 0.00199, -2.0, 0.0059], dtype=np.float32)
+    bad, worst = oracle.check(yref, S, ok, lib=lib)
+    assert bad == 0, bad
+    assert 0.0019 < worst <= 0.002, worst
+    for i, v in [(0, 1.0 + 0.021), (1, 1e-30), (2, 1.0), (3, np.inf), (4, -2.0025),
+                 (5, 0.0061)]:
+        t = ok.copy()
+        t[i] = v
+        bad, _ = oracle.check(yref, S, t, lib=lib)
+        assert bad == 1, (i, v, bad)
+
+
+def pin_synth_roundtrip(lib):
+    """The generator's quantised bytes dequantise back near the bf16 weights it
+    drew: |w - dequant(q)| <= half an e2m1 step at the block scale (a check of
+    the quantiser against the oracle's decoders, on a small matrix)."""
+    m = synth.nvfp4_normal_matrix(77, 1, 8, 64, threads=1)
+    wbits = synth.normal_bf16(77, 1, 8 * 64, std=synth.WEIGHT_STD, threads=1).reshape(8, 64)
+    w = torch_bf16(wbits)
+    for n in range(8):
+        d = oracle.dequant_row(m.codes[n], m.scales[n], 64, m.g, lib)
+        s = np.repeat([oracle.e4m3(int(b), lib) for b in m.scales[n]], 16) * m.g
+        # largest e2m1 gap is 2 (between 4 and 6); clamp at 6 adds at most (6.x-6)
+        assert (np.abs(w[n] - d) <= 1.0 * s + 1e-12).all()
+
+
+ALL_PINS = [pin_e2m1_table, pin_e4m3_torch, pin_e4m3_landmarks, pin_bf16_torch,
+            pin_dequant_rows, pin_exact_tiny_fast, pin_abs_sum, pin_one_hot,
+            pin_invariants, pin_nan_scale, pin_check]

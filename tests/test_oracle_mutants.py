@@ -1,0 +1,68 @@
+"""Plant plausible mistakes in a copy of the oracle and check that the pins
+catch every one of them (mutation testing, CPU only).
+
+Each mutant is the oracle source with one textual substitution, compiled with
+gcc into a temporary directory.  The real oracle source is never modified.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+import pins
+
+MUTANTS = {
+    "nibble_order_swapped": ("(k % 2 == 0) ? (byte & 0x0Fu) : (byte >> 4)",
+                             "(k % 2 == 0) ? (byte >> 4) : (byte & 0x0Fu)", 1),
+    "scale_block_32": ("scales_row[k / 16]", "scales_row[k / 32]", 1),
+    "scale_block_off_by_one": ("scales_row[k / 16]", "scales_row[(k + 1) / 16 < K / 16 ? (k + 1) / 16 : k / 16]", 1),
+    "e4m3_fnuz_bias": ("(int)e - 7);", "(int)e - 8);", 1),
+    "e4m3_subnormal_scale": ("ldexp((double)m, -9)", "ldexp((double)m, -10)", 1),
+    "e4m3_subnormal_as_normal": ("mag = ldexp((double)m, -9);", "mag = ldexp(1.0 + (double)m / 8.0, -6);", 1),
+    "e4m3_nan_dropped": ("if (e == 15 && m == 7)", "if (0)", 1),
+    "e4m3_mantissa_width": ("(double)m / 8.0", "(double)m / 16.0", 1),
+    "e2m1_subnormal": ("mag = 0.5 * (double)m;", "mag = 1.0 * (double)m;", 1),
+    "e2m1_bias": ("(int)e - 1);", "(int)e);", 1),
+    "e2m1_sign_dropped": ("return sign ? -mag : mag;", "return mag;", 1),
+    "e4m3_sign_dropped": ("return sign ? -mag : mag;\n}\n\n/* bf16", "return mag;\n}\n\n/* bf16", 1),
+    "global_scale_dropped": ("* s * g;", "* s;", 1),
+    "global_scale_divides": ("* s * g;", "* s / g;", 1),
+    "codes_row_stride": ("j->codes + n * (j->K / 2)", "j->codes + n * (j->K / 4)", 1),
+    "scales_row_stride": ("j->scales + n * (j->K / 16)", "j->scales + n * (j->K / 32)", 1),
+    "x_transposed": ("const double *xm = xd + m * j->K;", "const double *xm = xd + m;", 1),
+    "abs_dropped": ("absacc += fabs(t);", "absacc += t;", 1),
+    "last_k_dropped": ("for (int64_t k = 0; k < j->K; ++k) {\n                double t",
+                       "for (int64_t k = 0; k < j->K - 1; ++k) {\n                double t", 1),
+    "bf16_shift": ("(uint32_t)bits << 16", "(uint32_t)bits << 15", 1),
+    "output_index": ("j->y[m * j->nrows + r] = acc;", "j->y[r * j->M + m] = acc;", 1),
+    "check_signed_diff": ("double d = fabs(v - r);", "double d = v - r;", 1),
+    "check_zero_base": ("if (v != 0.0)\n                ++bad;", "if (0)\n                ++bad;", 1),
+    "check_nan": ("if (!isnan(v))\n                ++bad;", "if (0)\n                ++bad;", 1),
+}
+
+
+@pytest.fixture(scope="module")
+def source():
+    with open(oracle.SRC) as f:
+        return f.read()
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_mutant_is_caught(name, source, tmp_path):
+    old, new, count = MUTANTS[name]
+    assert source.count(old) >= count, f"mutation site for {name} not found in oracle.c"
+    mutated = source.replace(old, new, count)
+    assert mutated != source
+    src = tmp_path / "oracle_mut.c"
+    src.write_text(mutated)
+    out = str(tmp_path / f"liboracle_{name}.so")
+    oracle.build(str(src), out)
+    lib = oracle.load(out)
+    failures = []
+    for pin in pins.ALL_PINS:
+        try:
+            pin(lib)
+        except AssertionError:
+            failures.append(pin.__name__)
+    assert failures, f"no pin caught the planted mistake {name}"
