@@ -1,0 +1,142 @@
+/*
+ * q4proj.h — NVFP4 weight-only linear projection on AMD MI355X (gfx950).
+ *
+ *     y[m][n] = sum_k x[m][k] * W[n][k],    W[n][k] = e2m1(q[n][k]) * e4m3(s[n][k/16]) * g
+ *
+ * The operation is the projection behind the batch-one NVFP4 runners described
+ * on the Qwen3x-Orin README (section "Functional evaluation quick start": the
+ * SM87 projection backend with 512-row prefill chunks) and on the FlashRT
+ * "Qwen3.6 NVFP4 usage" page (speculative decoding section: verify runs K+1
+ * rows at once, 1 <= K <= 15; plain decode section: one row per step).  The
+ * weight format is the compressed-tensors NVFP4 checkpoint named in that
+ * page's constructor-argument table: e2m1 codes two per byte, one fp8-e4m3
+ * scale per 16 consecutive k, one fp32 per-tensor global scale g.
+ *
+ * Element formats.  e2m1 per the OCP Microscaling Formats v1.0 FP4 element
+ * (values 0, .5, 1, 1.5, 2, 3, 4, 6 and their negatives); e4m3 per the OCP
+ * 8-bit floating point spec, "fn" variant (bias 7, max 448, S.1111.111 = NaN,
+ * no infinities).  A NaN block scale makes every output of its row NaN.
+ *
+ * Canonical (caller) layouts, all row-major and densely packed:
+ *     codes   uint8   [N][K/2]   element 2j in bits 3:0, element 2j+1 in bits 7:4
+ *     scales  uint8   [N][K/16]  e4m3 bit patterns
+ *     x       uint16  [M][K]     bf16 bit patterns
+ *     y       float   [M][N]
+ *
+ * Conventions for every entry point:
+ *   - Pointers are DEVICE pointers owned by the caller; the library neither
+ *     allocates nor frees memory, keeps no state between calls except a cached
+ *     device check, and is reentrant.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  Calls
+ *     enqueue work on it and return without synchronising.
+ *   - Arguments are validated on the host before anything is launched; on any
+ *     error nothing is enqueued and a status code is returned.
+ *   - Outputs must not alias inputs.
+ *   - The weight is packed once (q4proj_pack, the one-time weight swizzle done
+ *     at construction on the FlashRT page); every projection reads the packed
+ *     form, and gemv and gemm read the same packed buffers.
+ */
+#ifndef Q4PROJ_H
+#define Q4PROJ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    Q4P_OK = 0,
+    Q4P_EINVAL = 1,       /* null pointer, non-positive size, K % 16 != 0, misalignment */
+    Q4P_EUNSUPPORTED = 2, /* valid arguments outside an entry point's range (gemv M > 16) */
+    Q4P_EDEVICE = 3,      /* current device is not gfx950, or no device */
+    Q4P_EWORKSPACE = 4,   /* workspace smaller than q4proj_workspace_bytes() */
+    Q4P_EHIP = 5          /* the HIP runtime reported an error at launch */
+} q4proj_status;
+
+/* Largest M accepted by q4proj_gemv: the verify shape K+1 with K <= 15. */
+#define Q4PROJ_GEMV_MAX_M 16
+
+/*
+ * Sizes of the packed buffers for an N x K weight (0 if N <= 0, K <= 0 or
+ * K % 16 != 0).  The packed layout pads N up to a multiple of 16 and K up to a
+ * multiple of 128 with zero codes and zero scales:
+ *     packed codes  = ceil(N/16) * ceil(K/128) * 1024 bytes  (>= N*K/2)
+ *     packed scales = ceil(N/16) * ceil(K/128) * 128 bytes   (>= N*K/16)
+ * The layout itself is private to the library; only q4proj_unpack reads it
+ * back out.
+ */
+size_t q4proj_packed_codes_bytes(int64_t N, int64_t K);
+size_t q4proj_packed_scales_bytes(int64_t N, int64_t K);
+
+/*
+ * Device scratch a projection needs for (M, N, K).  Every kernel of this
+ * library reduces in registers and LDS, so this is 0 for every valid shape;
+ * workspace may then be NULL.  The arguments stay in the projection entry
+ * points so that a future split-K kernel can use them without an ABI change.
+ */
+size_t q4proj_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * q4proj_pack — the one-time weight swizzle.
+ * In:  codes [N][K/2] and scales [N][K/16] in the canonical layout above.
+ * Out: packed_codes (q4proj_packed_codes_bytes(N,K) bytes) and packed_scales
+ *      (q4proj_packed_scales_bytes(N,K) bytes), laid out for 128-bit,
+ *      wave-contiguous loads by the projection kernels.  Padding is written
+ *      with zeros.  A pure byte permutation: no value is decoded or changed.
+ * Errors: EINVAL (null pointer, N <= 0, K <= 0, K % 16 != 0, in-place call),
+ *         EDEVICE, EHIP.
+ */
+q4proj_status q4proj_pack(const uint8_t *codes, const uint8_t *scales, int64_t N,
+                          int64_t K, uint8_t *packed_codes, uint8_t *packed_scales,
+                          void *stream);
+
+/*
+ * q4proj_unpack — exact inverse of q4proj_pack (padding is dropped).
+ * Errors: as q4proj_pack.
+ */
+q4proj_status q4proj_unpack(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                            int64_t N, int64_t K, uint8_t *codes, uint8_t *scales,
+                            void *stream);
+
+/*
+ * q4proj_gemv — decode and speculative-verify projection, 1 <= M <= 16.
+ *     y[M][N] (fp32) = x[M][K] (bf16) . dequant(W)^T, fp32 accumulation.
+ * Streams the packed weight once.  Each 16-element block's partial sum is
+ * formed from the unscaled e2m1 values and multiplied by its e4m3 scale; g is
+ * applied once per output after accumulation.  Deterministic: the same inputs
+ * give the same bits on every call.
+ * x must be 16-byte aligned (K % 16 == 0 keeps every row aligned).
+ * Errors: EINVAL (null pointer, M/N/K <= 0, K % 16 != 0, misaligned x),
+ *         EUNSUPPORTED (M > 16), EWORKSPACE, EDEVICE, EHIP.
+ */
+q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                          float global_scale, const uint16_t *x, float *y, int64_t M,
+                          int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * q4proj_gemm — prefill-chunk projection, any M >= 1 (sized for M = 512).
+ * Same arguments and result definition as q4proj_gemv.  Dequantises weight
+ * tiles to bf16 (exactly: q*s has at most 6 significant bits) and runs bf16
+ * matrix-core instructions with fp32 accumulation; g is applied once per
+ * output after accumulation.  Deterministic.
+ * Errors: EINVAL, EWORKSPACE, EDEVICE, EHIP.
+ */
+q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                          float global_scale, const uint16_t *x, float *y, int64_t M,
+                          int64_t N, int64_t K, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/* Human-readable name of a status code (static storage, never NULL). */
+const char *q4proj_status_string(q4proj_status s);
+
+/* Last HIP error string recorded by a Q4P_EHIP return on this thread. */
+const char *q4proj_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* Q4PROJ_H */

@@ -1,0 +1,179 @@
+"""Python binding of the q4proj C ABI (include/q4proj.h).
+
+Argument marshalling only: every function checks dtypes, devices, shapes and
+contiguity of torch tensors, then calls the entry point of the same name in
+``libq4proj.so`` on the current HIP stream.  All arithmetic runs in the HIP
+kernels; there is no fallback path.  Importing this module raises if the
+library has not been built (``python -m nvfp4_weight_only_q4proj_amd._build``
+or ``__graft_entry__.build()``).
+
+The projection computed is
+
+    y[m][n] = sum_k x[m][k] * e2m1(codes[n][k]) * e4m3(scales[n][k//16]) * g
+
+with codes packed two per byte (element 2j in the low nibble), bf16 x,
+fp32 y and fp32 global scale g.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libq4proj.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it with "
+                      "`python -m nvfp4_weight_only_q4proj_amd._build` (gfx950 only)")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_i64, _sz, _vp, _f32 = ctypes.c_int64, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+_lib.q4proj_packed_codes_bytes.argtypes = [_i64, _i64]
+_lib.q4proj_packed_codes_bytes.restype = _sz
+_lib.q4proj_packed_scales_bytes.argtypes = [_i64, _i64]
+_lib.q4proj_packed_scales_bytes.restype = _sz
+_lib.q4proj_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.q4proj_workspace_bytes.restype = _sz
+_lib.q4proj_pack.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
+_lib.q4proj_pack.restype = ctypes.c_int
+_lib.q4proj_unpack.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
+_lib.q4proj_unpack.restype = ctypes.c_int
+_PROJ_ARGS = [_vp, _vp, _f32, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]
+_lib.q4proj_gemv.argtypes = _PROJ_ARGS
+_lib.q4proj_gemv.restype = ctypes.c_int
+_lib.q4proj_gemm.argtypes = _PROJ_ARGS
+_lib.q4proj_gemm.restype = ctypes.c_int
+_lib.q4proj_status_string.argtypes = [ctypes.c_int]
+_lib.q4proj_status_string.restype = ctypes.c_char_p
+_lib.q4proj_last_hip_error.argtypes = []
+_lib.q4proj_last_hip_error.restype = ctypes.c_char_p
+
+#: Exported symbols declared by include/q4proj.h.
+SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
+           "q4proj_pack", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
+           "q4proj_status_string", "q4proj_last_hip_error")
+
+OK, EINVAL, EUNSUPPORTED, EDEVICE, EWORKSPACE, EHIP = range(6)
+GEMV_MAX_M = 16
+
+
+class Q4ProjError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        msg = _lib.q4proj_status_string(status).decode()
+        if status == EHIP:
+            msg += ": " + _lib.q4proj_last_hip_error().decode()
+        super().__init__(f"{where}: {msg}")
+        self.status = status
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise Q4ProjError(status, where)
+
+
+def library():
+    """The loaded ctypes library (for callers that want the raw C ABI)."""
+    return _lib
+
+
+def q4proj_packed_codes_bytes(N: int, K: int) -> int:
+    return int(_lib.q4proj_packed_codes_bytes(N, K))
+
+
+def q4proj_packed_scales_bytes(N: int, K: int) -> int:
+    return int(_lib.q4proj_packed_scales_bytes(N, K))
+
+
+def q4proj_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.q4proj_workspace_bytes(M, N, K))
+
+
+def _stream(t: torch.Tensor, stream):
+    if stream is None:
+        stream = torch.cuda.current_stream(t.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, dtype, numel: int, device):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.device.type != "cuda" or (device is not None and t.device != device):
+        raise ValueError(f"{name} must be on {device or 'a HIP device'}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() != numel:
+        raise ValueError(f"{name} must have {numel} elements, got {t.numel()}")
+
+
+def q4proj_pack(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int,
+                packed_codes: torch.Tensor, packed_scales: torch.Tensor, stream=None) -> None:
+    """codes u8 [N][K/2], scales u8 [N][K/16] -> packed buffers (u8, sizes from
+    q4proj_packed_*_bytes)."""
+    dev = codes.device
+    _need(codes, "codes", torch.uint8, N * (K // 2), dev)
+    _need(scales, "scales", torch.uint8, N * (K // 16), dev)
+    _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
+    _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
+    with torch.cuda.device(dev):
+        _check(_lib.q4proj_pack(codes.data_ptr(), scales.data_ptr(), N, K, packed_codes.data_ptr(),
+                                packed_scales.data_ptr(), _stream(codes, stream)), "q4proj_pack")
+
+
+def q4proj_unpack(packed_codes: torch.Tensor, packed_scales: torch.Tensor, N: int, K: int,
+                  codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
+    dev = packed_codes.device
+    _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
+    _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
+    _need(codes, "codes", torch.uint8, N * (K // 2), dev)
+    _need(scales, "scales", torch.uint8, N * (K // 16), dev)
+    with torch.cuda.device(dev):
+        _check(_lib.q4proj_unpack(packed_codes.data_ptr(), packed_scales.data_ptr(), N, K,
+                                  codes.data_ptr(), scales.data_ptr(), _stream(codes, stream)),
+               "q4proj_unpack")
+
+
+def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, workspace, stream):
+    dev = x.device
+    _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
+    _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
+    if x.dtype == torch.bfloat16:
+        x = x.view(torch.int16)
+    if x.dtype not in (torch.int16, torch.uint16):
+        raise TypeError(f"x must hold bf16 (bfloat16 or 16-bit bit patterns), got {x.dtype}")
+    _need(x, "x", x.dtype, M * K, dev)
+    _need(y, "y", torch.float32, M * N, dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    with torch.cuda.device(dev):
+        _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
+                  x.data_ptr(), y.data_ptr(), M, N, K, ws_ptr, ws_bytes, _stream(x, stream)),
+               where)
+
+
+def q4proj_gemv(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,
+                workspace=None, stream=None) -> None:
+    """y[M][N] fp32 = x[M][K] bf16 . dequant(W)^T for 1 <= M <= 16."""
+    _proj(_lib.q4proj_gemv, "q4proj_gemv", packed_codes, packed_scales, global_scale, x, y, M, N,
+          K, workspace, stream)
+
+
+def q4proj_gemm(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,
+                workspace=None, stream=None) -> None:
+    """y[M][N] fp32 = x[M][K] bf16 . dequant(W)^T for any M >= 1."""
+    _proj(_lib.q4proj_gemm, "q4proj_gemm", packed_codes, packed_scales, global_scale, x, y, M, N,
+          K, workspace, stream)
+
+
+def pack_weight(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, stream=None):
+    """Allocate packed buffers on codes.device and fill them with q4proj_pack."""
+    pc = torch.empty(q4proj_packed_codes_bytes(N, K), dtype=torch.uint8, device=codes.device)
+    ps = torch.empty(q4proj_packed_scales_bytes(N, K), dtype=torch.uint8, device=codes.device)
+    q4proj_pack(codes, scales, N, K, pc, ps, stream)
+    return pc, ps

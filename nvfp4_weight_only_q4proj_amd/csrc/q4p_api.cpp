@@ -1,0 +1,206 @@
+// q4p_api.cpp — the C ABI of include/q4proj.h: argument validation, the
+// gfx950 device check, and dispatch to the kernel launchers.
+//
+// Every argument check runs on the host before any HIP call, so a rejected
+// call enqueues nothing and touches no device.  The device check runs next
+// and is cached per device ordinal.
+#include "q4proj.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstring>
+
+#include "q4p_launch.h"
+#include "q4p_layout.h"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_ok[kMaxDevices];   // 0 unknown, 1 gfx950, -1 other
+
+thread_local char g_last_hip_error[256] = "";
+
+q4proj_status record_hip(hipError_t e)
+{
+    if (e == hipSuccess)
+        return Q4P_OK;
+    const char *s = hipGetErrorString(e);
+    std::strncpy(g_last_hip_error, s ? s : "unknown HIP error", sizeof g_last_hip_error - 1);
+    g_last_hip_error[sizeof g_last_hip_error - 1] = '\0';
+    return Q4P_EHIP;
+}
+
+// The library carries gfx950 code objects only and refuses every other device
+// instead of falling back to another path.
+q4proj_status check_device()
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return Q4P_EDEVICE;
+    if (dev < kMaxDevices) {
+        int known = g_device_ok[dev].load(std::memory_order_relaxed);
+        if (known != 0)
+            return known > 0 ? Q4P_OK : Q4P_EDEVICE;
+    }
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess)
+        return Q4P_EDEVICE;
+    const bool ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0;
+    if (dev < kMaxDevices)
+        g_device_ok[dev].store(ok ? 1 : -1, std::memory_order_relaxed);
+    return ok ? Q4P_OK : Q4P_EDEVICE;
+}
+
+bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool shape_ok(int64_t N, int64_t K)
+{
+    // sizes the kernels index with 32-bit ints
+    return N > 0 && K > 0 && K % 16 == 0 && N <= (int64_t)1 << 30 && K <= (int64_t)1 << 24;
+}
+
+bool overlap(const void *a, size_t na, const void *b, size_t nb)
+{
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+q4proj_status check_projection(const uint8_t *pc, const uint8_t *ps, const uint16_t *x,
+                               const float *y, int64_t M, int64_t N, int64_t K,
+                               size_t workspace_bytes)
+{
+    if (!pc || !ps || !x || !y)
+        return Q4P_EINVAL;
+    if (M <= 0 || !shape_ok(N, K) || M > (int64_t)1 << 24)
+        return Q4P_EINVAL;
+    if ((uint64_t)M * (uint64_t)N > ((uint64_t)1 << 40))
+        return Q4P_EINVAL;
+    if (!aligned(pc, 16) || !aligned(ps, 8) || !aligned(x, 16) || !aligned(y, 4))
+        return Q4P_EINVAL;
+    const size_t ybytes = (size_t)M * (size_t)N * sizeof(float);
+    if (overlap(y, ybytes, x, (size_t)M * (size_t)K * 2) ||
+        overlap(y, ybytes, pc, q4proj_packed_codes_bytes(N, K)) ||
+        overlap(y, ybytes, ps, q4proj_packed_scales_bytes(N, K)))
+        return Q4P_EINVAL;
+    if (workspace_bytes < q4proj_workspace_bytes(M, N, K))
+        return Q4P_EWORKSPACE;
+    return Q4P_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t q4proj_packed_codes_bytes(int64_t N, int64_t K)
+{
+    if (!shape_ok(N, K))
+        return 0;
+    return (size_t)(q4p::n_tiles(N) * q4p::k_tiles(K)) * q4p::kTileCodeBytes;
+}
+
+size_t q4proj_packed_scales_bytes(int64_t N, int64_t K)
+{
+    if (!shape_ok(N, K))
+        return 0;
+    return (size_t)(q4p::n_tiles(N) * q4p::k_tiles(K)) * q4p::kTileScaleBytes;
+}
+
+size_t q4proj_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    (void)M;
+    (void)N;
+    (void)K;
+    return 0;
+}
+
+q4proj_status q4proj_pack(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                          uint8_t *packed_codes, uint8_t *packed_scales, void *stream)
+{
+    if (!codes || !scales || !packed_codes || !packed_scales || !shape_ok(N, K))
+        return Q4P_EINVAL;
+    if (!aligned(codes, 8) || !aligned(packed_codes, 16) || !aligned(packed_scales, 8))
+        return Q4P_EINVAL;
+    const size_t pcb = q4proj_packed_codes_bytes(N, K), psb = q4proj_packed_scales_bytes(N, K);
+    const size_t cb = (size_t)N * (size_t)(K / 2), sb = (size_t)N * (size_t)(K / 16);
+    if (overlap(packed_codes, pcb, codes, cb) || overlap(packed_codes, pcb, scales, sb) ||
+        overlap(packed_scales, psb, codes, cb) || overlap(packed_scales, psb, scales, sb) ||
+        overlap(packed_codes, pcb, packed_scales, psb))
+        return Q4P_EINVAL;
+    q4proj_status st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_pack(codes, scales, N, K, packed_codes, packed_scales,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+q4proj_status q4proj_unpack(const uint8_t *packed_codes, const uint8_t *packed_scales, int64_t N,
+                            int64_t K, uint8_t *codes, uint8_t *scales, void *stream)
+{
+    if (!codes || !scales || !packed_codes || !packed_scales || !shape_ok(N, K))
+        return Q4P_EINVAL;
+    if (!aligned(codes, 8) || !aligned(packed_codes, 16) || !aligned(packed_scales, 8))
+        return Q4P_EINVAL;
+    const size_t pcb = q4proj_packed_codes_bytes(N, K), psb = q4proj_packed_scales_bytes(N, K);
+    const size_t cb = (size_t)N * (size_t)(K / 2), sb = (size_t)N * (size_t)(K / 16);
+    if (overlap(packed_codes, pcb, codes, cb) || overlap(packed_codes, pcb, scales, sb) ||
+        overlap(packed_scales, psb, codes, cb) || overlap(packed_scales, psb, scales, sb) ||
+        overlap(codes, cb, scales, sb))
+        return Q4P_EINVAL;
+    q4proj_status st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_unpack(packed_codes, packed_scales, N, K, codes, scales,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                          float global_scale, const uint16_t *x, float *y, int64_t M, int64_t N,
+                          int64_t K, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    q4proj_status st = check_projection(packed_codes, packed_scales, x, y, M, N, K,
+                                        workspace_bytes);
+    if (st != Q4P_OK)
+        return st;
+    if (M > Q4PROJ_GEMV_MAX_M)
+        return Q4P_EUNSUPPORTED;
+    st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_gemv(packed_codes, packed_scales, global_scale, x, y, M, N, K,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                          float global_scale, const uint16_t *x, float *y, int64_t M, int64_t N,
+                          int64_t K, void *workspace, size_t workspace_bytes, void *stream)
+{
+    (void)workspace;
+    q4proj_status st = check_projection(packed_codes, packed_scales, x, y, M, N, K,
+                                        workspace_bytes);
+    if (st != Q4P_OK)
+        return st;
+    st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_gemm(packed_codes, packed_scales, global_scale, x, y, M, N, K,
+                                       static_cast<hipStream_t>(stream)));
+}
+
+const char *q4proj_status_string(q4proj_status s)
+{
+    switch (s) {
+    case Q4P_OK: return "Q4P_OK";
+    case Q4P_EINVAL: return "Q4P_EINVAL: invalid argument";
+    case Q4P_EUNSUPPORTED: return "Q4P_EUNSUPPORTED: arguments outside this entry point's range";
+    case Q4P_EDEVICE: return "Q4P_EDEVICE: current device is not gfx950";
+    case Q4P_EWORKSPACE: return "Q4P_EWORKSPACE: workspace too small";
+    case Q4P_EHIP: return "Q4P_EHIP: HIP runtime error";
+    }
+    return "unknown q4proj_status";
+}
+
+const char *q4proj_last_hip_error(void) { return g_last_hip_error; }
+
+}  // extern "C"

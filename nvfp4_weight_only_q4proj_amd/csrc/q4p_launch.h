@@ -1,0 +1,25 @@
+// q4p_launch.h — kernel launchers behind the C ABI (internal).
+// Arguments are validated by the caller (q4p_api.cpp); launchers only size the
+// grid, enqueue on `stream` and return hipGetLastError().
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace q4p {
+
+hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
+                       uint8_t *packed_codes, uint8_t *packed_scales, hipStream_t stream);
+
+hipError_t launch_unpack(const uint8_t *packed_codes, const uint8_t *packed_scales, int64_t N,
+                         int64_t K, uint8_t *codes, uint8_t *scales, hipStream_t stream);
+
+hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
+                       const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t stream);
+
+hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
+                       const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t stream);
+
+}  // namespace q4p

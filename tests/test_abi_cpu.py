@@ -1,0 +1,118 @@
+"""The C-ABI library on the CPU: it loads, exports every declared symbol, sizes
+the packed layout, and rejects bad arguments on the host before touching a
+device.  No projection is computed here."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "q4proj.h")
+
+
+@pytest.fixture(scope="module")
+def q4():
+    import nvfp4_weight_only_q4proj_amd as q4
+    return q4
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(q4proj_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol(q4):
+    names = declared_functions()
+    assert len(names) == 9, names
+    lib = q4.library()
+    for name in names:
+        assert hasattr(lib, name), name
+    assert sorted(q4.SYMBOLS) == names
+
+
+def test_library_is_gfx950_only():
+    # the shared object carries a gfx950 code object and no other GPU target
+    data = open(os.path.join(ROOT, "nvfp4_weight_only_q4proj_amd", "libq4proj.so"), "rb").read()
+    assert b"gfx950" in data
+    for other in (b"gfx942", b"gfx90a", b"gfx1100", b"sm_"):
+        assert b"amdgcn-amd-amdhsa--" + other not in data
+
+
+@pytest.mark.parametrize("N,K", [(1, 16), (16, 128), (17, 144), (512, 256), (17408, 5120),
+                                 (5120, 17408), (248320, 5120), (2560, 9216)])
+def test_packed_sizes(q4, N, K):
+    nt, kt = -(-N // 16), -(-K // 128)
+    assert q4.q4proj_packed_codes_bytes(N, K) == nt * kt * 1024 >= N * K // 2
+    assert q4.q4proj_packed_scales_bytes(N, K) == nt * kt * 128 >= N * K // 16
+    assert q4.q4proj_workspace_bytes(7, N, K) == 0
+
+
+@pytest.mark.parametrize("N,K", [(0, 16), (16, 0), (16, 8), (16, 24), (-1, 16)])
+def test_packed_sizes_invalid(q4, N, K):
+    assert q4.q4proj_packed_codes_bytes(N, K) == 0
+    assert q4.q4proj_packed_scales_bytes(N, K) == 0
+
+
+# Fake, well-aligned, non-overlapping addresses: every call below must be
+# rejected by the host-side checks before any HIP call is made.
+A, B, X, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+
+
+def proj(lib, fn, pc=A, ps=B, x=X, y=Y, M=1, N=64, K=256, ws=None, wsb=0):
+    return getattr(lib, fn)(pc, ps, ctypes.c_float(1.0), x, y, M, N, K, ws, wsb, None)
+
+
+@pytest.mark.parametrize("fn", ["q4proj_gemv", "q4proj_gemm"])
+def test_projection_validation(q4, fn):
+    lib = q4.library()
+    assert proj(lib, fn, pc=None) == q4.EINVAL
+    assert proj(lib, fn, ps=None) == q4.EINVAL
+    assert proj(lib, fn, x=None) == q4.EINVAL
+    assert proj(lib, fn, y=None) == q4.EINVAL
+    assert proj(lib, fn, M=0) == q4.EINVAL
+    assert proj(lib, fn, N=0) == q4.EINVAL
+    assert proj(lib, fn, K=0) == q4.EINVAL
+    assert proj(lib, fn, K=24) == q4.EINVAL          # K % 16 != 0
+    assert proj(lib, fn, M=-3) == q4.EINVAL
+    assert proj(lib, fn, x=X + 8) == q4.EINVAL       # x must be 16-byte aligned
+    assert proj(lib, fn, pc=A + 4) == q4.EINVAL
+    assert proj(lib, fn, y=Y + 2) == q4.EINVAL
+    assert proj(lib, fn, y=X + 64) == q4.EINVAL      # y overlaps x
+    assert proj(lib, fn, y=A) == q4.EINVAL           # y overlaps the packed codes
+
+
+def test_gemv_m_range(q4):
+    lib = q4.library()
+    assert proj(lib, "q4proj_gemv", M=17) == q4.EUNSUPPORTED
+    assert proj(lib, "q4proj_gemv", M=1000) == q4.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("fn", ["q4proj_pack", "q4proj_unpack"])
+def test_pack_validation(q4, fn):
+    lib = q4.library()
+    f = getattr(lib, fn)
+    assert f(None, B, 16, 128, X, Y, None) == q4.EINVAL
+    assert f(A, None, 16, 128, X, Y, None) == q4.EINVAL
+    assert f(A, B, 16, 120, X, Y, None) == q4.EINVAL
+    assert f(A, B, 0, 128, X, Y, None) == q4.EINVAL
+    assert f(A, B, 16, 128, A, Y, None) == q4.EINVAL   # in place
+    assert f(A, B, 16, 128, X + 4, Y, None) == q4.EINVAL
+
+
+def test_status_strings(q4):
+    lib = q4.library()
+    for s in range(6):
+        assert lib.q4proj_status_string(s).decode().startswith("Q4P_")
+    assert b"unknown" in lib.q4proj_status_string(99)
+
+
+@pytest.mark.skipif(__import__("torch").cuda.is_available(), reason="needs a host without a GPU")
+def test_no_device_no_fallback(q4):
+    """With valid arguments and no gfx950 device the library refuses (EDEVICE)
+    instead of computing anything elsewhere."""
+    lib = q4.library()
+    assert proj(lib, "q4proj_gemv") == q4.EDEVICE
+    assert proj(lib, "q4proj_gemm", M=512) == q4.EDEVICE
+    assert lib.q4proj_pack(A, B, 16, 128, X, Y, None) == q4.EDEVICE
