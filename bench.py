@@ -1,0 +1,323 @@
+"""Benchmark of the NVFP4 weight-only projection on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one decode pass of the 27B-style dense MLP at M = 1: the gate/up
+GEMV (K=5120 -> N=17408) followed by the down GEMV (K=17408 -> N=5120), each
+through the C ABI on packed weights already resident in HBM.  `value` is the
+algorithmic bytes of the step (packed codes + e4m3 scales + x + y + g) per
+second.  Each step uses a different copy of the packed weights, cycling
+through >= 512 MB of copies, so the 256 MB Infinity Cache cannot serve them.
+
+Also measured and reported in the same JSON line:
+  roofline      the GEMV kernel: bytes per launch / mean launch duration (HIP
+                events around every launch on the launch stream) vs 8 TB/s;
+                `traffic` from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary in
+                profiles/ when it was taken on the current kernel source.
+  prefill_gemm  the M = 512 prefill chunk (qkv 5120->14336, gate/up
+                5120->17408): TFLOP/s vs 2.517 PFLOP/s dense bf16.
+  shapes        the other workloads' GEMVs (M = 7 verify, lm-head, 4B shapes).
+  pack          the one-time weight swizzle (read + write bytes / s).
+  cpu_baseline  the CPU oracle on the decode step, on the host cores.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2517.0          # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+MALL_DEFEAT_BYTES = 512 << 20
+METRIC = "NVFP4 projection GB/s & % HBM peak (M=1); TFLOP/s & % MFMA peak (M=512)"
+
+
+def algo_bytes(M, N, K):
+    """Packed codes + e4m3 scales + bf16 x + fp32 y + the fp32 global scale."""
+    return N * K // 2 + N * K // 16 + 2 * M * K + 4 * M * N + 4
+
+
+def src_digest(name):
+    path = os.path.join(ROOT, "nvfp4_weight_only_q4proj_amd", "csrc", name)
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def read_traffic(profile, digest, launch_bytes):
+    """HBM bytes per launch from a committed rocprofv3 counter summary, or None
+    when absent or taken on other kernel source."""
+    path = os.path.join(ROOT, "profiles", profile)
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.lstrip().startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("kernel_source_sha256_16") != digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def head_start(torch, ms):
+    """Queue a spin kernel so the host can enqueue the timed launches while
+    the GPU is busy: the timed region then measures back-to-back kernels,
+    not the host's launch rate."""
+    torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
+
+
+class Timed:
+    """HIP events around every launch, on the stream the launch uses."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __call__(self, tag, fn):
+        s = self.torch.cuda.Event(enable_timing=True)
+        e = self.torch.cuda.Event(enable_timing=True)
+        s.record()
+        fn()
+        e.record()
+        self.pairs.append((tag, s, e))
+
+    def ms(self, tag):
+        return sum(s.elapsed_time(e) for t, s, e in self.pairs if t == tag)
+
+    def count(self, tag):
+        return sum(1 for t, _, _ in self.pairs if t == tag)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--skip-cpu", action="store_true", help="omit the cpu_baseline leg")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="wall-time bound of the cpu_baseline sample")
+    ap.add_argument("--only", choices=["dec", "pre", "all"], default="all",
+                    help="restrict the run (for profiling one kernel)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run a plain 256 MiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(the projection shards by output columns or by k; see DESIGN.md).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import nvfp4_weight_only_q4proj_amd as q4
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    props = torch.cuda.get_device_properties(dev)
+
+    def upload(case, copies):
+        mat = case.matrix
+        codes = torch.from_numpy(mat.codes.reshape(-1)).to(dev)
+        scales = torch.from_numpy(mat.scales.reshape(-1)).to(dev)
+        pc, ps = q4.pack_weight(codes, scales, mat.N, mat.K)
+        reps = [(pc, ps)] + [(pc.clone(), ps.clone()) for _ in range(copies - 1)]
+        x = torch.from_numpy(case.x.view(np.int16)).to(dev)
+        y = torch.empty((case.M, mat.N), dtype=torch.float32, device=dev)
+        del codes, scales
+        return {"case": case, "w": reps, "x": x, "y": y, "g": mat.g}
+
+    def copies_for(step_bytes):
+        return max(2, -(-MALL_DEFEAT_BYTES // step_bytes))
+
+    def launcher(kind, u, i):
+        fn = q4.q4proj_gemv if kind == "gemv" else q4.q4proj_gemm
+        c = u["case"]
+        pc, ps = u["w"][i % len(u["w"])]
+        return lambda: fn(pc, ps, u["g"], u["x"], u["y"], c.M, c.N, c.K)
+
+    out = {"metric": METRIC}
+    timer = Timed(torch)
+
+    # ---- decode step: gate/up + down GEMV at M = 1 -------------------------
+    dec = synth.workload_cases("dec")
+    step_bytes = sum(algo_bytes(c.M, c.N, c.K) for c in dec)
+    ncopy = copies_for(step_bytes)
+    dec_u = [upload(c, ncopy) for c in dec]
+    torch.cuda.synchronize()
+
+    if args.only in ("dec", "all"):
+        for i in range(args.warmup):
+            for u in dec_u:
+                launcher("gemv", u, i)()
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        wall0 = time.perf_counter()
+        head_start(torch, 0.1 * args.steps + 5)
+        t0.record()
+        for i in range(args.steps):
+            for u in dec_u:
+                launcher("gemv", u, args.warmup + i)()
+        t1.record()
+        host_s = time.perf_counter() - wall0
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - wall0
+        step_ms = t0.elapsed_time(t1) / args.steps
+        # roofline pass: the same launches, each bracketed by HIP events on the
+        # launch stream, to get the kernel's mean duration per launch
+        head_start(torch, 0.1 * args.steps + 5)
+        for i in range(args.steps):
+            for u in dec_u:
+                timer("gemv", launcher("gemv", u, i))
+        torch.cuda.synchronize()
+        gemv_launches = timer.count("gemv")
+        gemv_ms = timer.ms("gemv") / gemv_launches
+        launch_bytes = step_bytes / len(dec_u)
+        achieved = launch_bytes / (gemv_ms * 1e-3) / 1e9
+        digest = src_digest("q4p_gemv.hip")
+        traffic = read_traffic("gemv_dec_traffic.txt", digest, launch_bytes)
+        value = step_bytes / (step_ms * 1e-3) / 1e9
+        out.update({
+            "value": round(value, 1), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": round(step_ms, 5), "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic (seeded N(0,0.02) bf16 weights, two-level NVFP4; x ~ N(0,1) bf16)",
+            "config": {"workload": "decode M=1, 27B-style MLP: gate/up 5120->17408 + down "
+                                   "17408->5120 NVFP4 GEMV",
+                       "M": 1, "shapes": [[c.N, c.K] for c in dec],
+                       "bytes_per_step": step_bytes, "weight_copies": ncopy,
+                       "rotation_bytes": ncopy * sum(
+                           u["w"][0][0].numel() + u["w"][0][1].numel() for u in dec_u)},
+            "tokens_per_s": round(1.0 / (step_ms * 1e-3), 1),
+            "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+            "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1>",
+                         "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic, "mean_launch_us": round(gemv_ms * 1e3, 3),
+                         "bytes_per_launch": launch_bytes,
+                         "kernel_source_sha256_16": digest},
+            "device": {"name": props.name, "cus": props.multi_processor_count,
+                       "arch": getattr(props, "gcnArchName", "")},
+            "wall_s_timed": round(wall, 4),
+            "host_enqueue_us_per_launch": round(host_s / (args.steps * len(dec_u)) * 1e6, 2),
+        })
+
+    # ---- prefill chunk: M = 512 GEMM --------------------------------------
+    if args.only in ("pre", "all"):
+        pre = synth.workload_cases("pre")
+        pre_bytes = sum(algo_bytes(c.M, c.N, c.K) for c in pre)
+        pre_u = [upload(c, copies_for(pre_bytes)) for c in pre]
+        torch.cuda.synchronize()
+        for i in range(max(3, args.warmup // 4)):
+            for u in pre_u:
+                launcher("gemm", u, i)()
+        torch.cuda.synchronize()
+        gsteps = max(10, args.steps // 4)
+        head_start(torch, 0.1 * gsteps + 5)
+        for i in range(gsteps):
+            for u in pre_u:
+                timer("gemm_" + u["case"].name, launcher("gemm", u, i))
+        torch.cuda.synchronize()
+        per = {}
+        tot_flop = tot_ms = 0.0
+        for u in pre_u:
+            c = u["case"]
+            ms = timer.ms("gemm_" + c.name) / gsteps
+            flop = 2.0 * c.M * c.N * c.K
+            tot_flop += flop
+            tot_ms += ms
+            per[c.name] = {"M": c.M, "N": c.N, "K": c.K, "us": round(ms * 1e3, 2),
+                           "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
+                           "mfma_frac": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+        tflops = tot_flop / (tot_ms * 1e-3) / 1e12
+        out["prefill_gemm"] = {
+            "workload": "prefill chunk M=512: qkv 5120->14336 + gate/up 5120->17408",
+            "tflops": round(tflops, 1), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(tflops, 1),
+                         "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
+                         "traffic": None, "kernel_source_sha256_16": src_digest("q4p_gemm.hip")},
+            "tokens_per_s": round(512 / (tot_ms * 1e-3), 1),
+            "per_matrix": per, "steps": gsteps}
+        del pre_u
+
+    # ---- the other decode-type shapes, the pack step ------------------------
+    if args.only == "all":
+        shapes = {}
+        for wl in ("mtp", "lmh"):
+            for c in synth.workload_cases(wl):
+                b = algo_bytes(c.M, c.N, c.K)
+                u = upload(c, copies_for(b))
+                n = max(10, args.steps // 4)
+                for i in range(3):
+                    launcher("gemv", u, i)()
+                head_start(torch, 0.1 * n + 5)
+                for i in range(n):
+                    timer(f"{wl}_{c.name}", launcher("gemv", u, i))
+                torch.cuda.synchronize()
+                ms = timer.ms(f"{wl}_{c.name}") / n
+                shapes[f"{wl}/{c.name}"] = {"M": c.M, "N": c.N, "K": c.K,
+                                            "us": round(ms * 1e3, 2),
+                                            "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                                            "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                del u
+        out["shapes"] = shapes
+        # pack: read canonical + write packed bytes of the lm-head weight
+        lm = synth.workload_cases("lmh", only=["lm_head"])[0].matrix
+        codes = torch.from_numpy(lm.codes.reshape(-1)).to(dev)
+        scales = torch.from_numpy(lm.scales.reshape(-1)).to(dev)
+        pc = torch.empty(q4.q4proj_packed_codes_bytes(lm.N, lm.K), dtype=torch.uint8, device=dev)
+        ps = torch.empty(q4.q4proj_packed_scales_bytes(lm.N, lm.K), dtype=torch.uint8, device=dev)
+        for i in range(2):
+            q4.q4proj_pack(codes, scales, lm.N, lm.K, pc, ps)
+        head_start(torch, 5)
+        for i in range(5):
+            timer("pack", lambda: q4.q4proj_pack(codes, scales, lm.N, lm.K, pc, ps))
+        torch.cuda.synchronize()
+        ms = timer.ms("pack") / 5
+        moved = codes.numel() + scales.numel() + pc.numel() + ps.numel()
+        out["pack"] = {"N": lm.N, "K": lm.K, "us": round(ms * 1e3, 1),
+                       "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
+        del codes, scales, pc, ps
+
+    if args.calibrate_copy:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+
+    # ---- CPU baseline: the oracle on the decode step ----------------------
+    if not args.skip_cpu and args.only in ("dec", "all"):
+        import oracle
+        nthreads = oracle.default_threads()
+        reps = 0
+        t = time.perf_counter()
+        while True:
+            for c in dec:
+                oracle.proj(c.matrix.codes, c.matrix.scales, c.matrix.g, c.x, nthreads=nthreads)
+            reps += 1
+            el = time.perf_counter() - t
+            if el >= args.cpu_seconds or reps >= 50:
+                break
+        out["cpu_baseline"] = {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s",
+                               "cores": nthreads, "kind": "oracle",
+                               "sample": f"{reps} full decode steps (gate/up + down, M=1, "
+                                         f"all rows) in {el:.2f} s, fp64",
+                               "tokens_per_s": round(reps / el, 2)}
+
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

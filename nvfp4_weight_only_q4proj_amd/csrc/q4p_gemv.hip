@@ -1,24 +1,41 @@
 // q4p_gemv.hip — decode / speculative-verify projection, 1 <= M <= 16.
 //
-// Shape of the problem: at M = 1..16 every weight byte is used by at most 16
-// multiply-adds, so the kernel is bound by streaming the packed weight from
-// HBM once (0.5625 bytes per weight).  Design:
+// At M = 1..16 every weight byte feeds at most 16 multiply-adds, so the
+// kernel is bound by streaming the packed weight from HBM once (0.5625 bytes
+// per weight).  Design:
 //
-//  * One workgroup per 16-row tile of W; its S waves split the k-tiles of
-//    that row tile evenly (split-K inside the workgroup), so short-N shapes
-//    still put enough waves on the chip.  Partial sums are combined through
-//    LDS in a fixed order: results are bitwise deterministic.
-//  * Each wave streams one 1 KB code tile + one 128 B scale tile per k-tile
-//    with 128-bit loads, PF k-tiles ahead in registers.
+//  * A workgroup owns TB 16-row tiles of W; S waves per tile split its
+//    k-tiles into contiguous ranges (split-K inside the workgroup), and the
+//    partial sums are added through LDS in a fixed order, so results are
+//    bitwise deterministic.  The host picks (TB, S) from the occupancy API so
+//    that, where possible, every workgroup is resident at once: no tail round.
+//  * Each wave keeps PF k-tiles in flight in a register ring: the 1 KB code
+//    tile (16 B per lane) and the 128 B scale tile (8 B per lane); every
+//    wave-wide weight load is a contiguous 1 KB segment.
 //  * Per 16-element scale block the wave issues one 16x16x16 bf16 MFMA:
-//    A = 16 activation rows (rows >= M are zero), B = the 16 weight rows'
-//    unscaled e2m1 values (exact in bf16).  The MFMA returns the block's
-//    partial sums p[m][n] = sum_{k in block} x[m][k] q[n][k]; the lane then
+//    A = activation rows (lane row r, k-group g holds 4 values), B = the 16
+//    weight rows' unscaled e2m1 values (exact in bf16).  The MFMA returns the
+//    block's partial sums p[m][n] = sum_{k in block} x[m][k] q[n][k]; the lane
 //    accumulates acc += s[n][block] * p with one fma per live output row.
-//    This keeps the per-weight vector work at one conversion per two codes;
-//    folding the e4m3 scale into the operand would cost two more multiplies
-//    because the hardware fp4 conversion honours only the scale's exponent.
+//    Folding the e4m3 scale into the operand instead would cost two more
+//    multiplies per code pair, because gfx950's fp4 conversion honours only
+//    the exponent of its scale operand.
+//  * Activations, when M*K fits (decode, lm-head): each wave copies the
+//    activations of its own k-range into LDS once, permuted so that a lane's
+//    32 values of a k-tile are 64 contiguous bytes (two 16-byte LDS reads per
+//    half tile); no workgroup barrier stands between a wave and its first
+//    tile.  Lanes whose A row is >= M read a zero strip.
+//  * Activations otherwise (larger M*K, e.g. verify with K = 17408): the
+//    pieces ride in the register ring with the weights.  A rows >= M only
+//    produce discarded output rows, so for small M one register pair holds
+//    the pieces of BPP blocks (lane m + M*t holds block t's piece of row m)
+//    and a DPP row shift by M*t moves block t's pieces into lanes 0..M-1
+//    just before its MFMA.  M <= 2 needs one pair per k-tile, M <= 4 two,
+//    M <= 8 four, larger M eight (no shifts).
 //  * g is applied once per output after the reduction, in fp32.
+#include <mutex>
+#include <vector>
+
 #include "q4p_device.h"
 #include "q4p_launch.h"
 
@@ -26,139 +43,429 @@ namespace q4p {
 
 namespace {
 
-constexpr int kMaxSplit = 8;       // waves per workgroup
-constexpr int kPrefetch = 4;       // k-tiles in flight per wave
+constexpr int kMaxWaves = 16;          // waves per workgroup
+constexpr int kZeroBytes = 64;         // zero strip for activation rows >= M
+constexpr int kXLdsMaxBytes = 40 * 1024;
+constexpr int kXStage = 8;             // staged activation groups per lane
 
-// Accumulate one k-tile.  R = number of accumulator rows per lane that hold
-// live outputs (min(M, 4)); rows beyond it only ever see zero activations.
-template <int R>
-__device__ __forceinline__ void gemv_tile(const uint4 &cw, const uint2 &sw, const uint2 (&xw)[8],
-                                          floatx4_t &acc)
+// Compile-time shape for M (MT = M for M <= 8, MT = 0 for 9 <= M <= 16).
+template <int MT, bool XLDS>
+struct Shape {
+    static constexpr int kPairs = XLDS ? 0 : MT == 0 ? 8 : MT <= 2 ? 1 : MT <= 4 ? 2 : 4;
+    static constexpr int kBpp = XLDS ? 1 : 8 / kPairs;          // blocks per pair
+    static constexpr int kRows = MT == 0 ? 4 : (MT < 4 ? MT : 4);   // live acc rows
+    static constexpr int kPrefetch = XLDS ? 6 : kPairs <= 1 ? 6 : kPairs <= 2 ? 5 : kPairs <= 4 ? 4 : 3;
+    static constexpr int kRing = kPairs > 0 ? kPairs : 1;
+};
+
+// row shift within each 16-lane DPP row: lane i <- lane i + SH
+template <int SH>
+__device__ __forceinline__ uint2 shift_rows(uint2 v)
 {
-    const uint32_t words[4] = {cw.x, cw.y, cw.z, cw.w};
+    if (SH == 0)
+        return v;
+    return make_uint2((uint32_t)__builtin_amdgcn_mov_dpp((int)v.x, 0x100 | SH, 0xF, 0xF, false),
+                      (uint32_t)__builtin_amdgcn_mov_dpp((int)v.y, 0x100 | SH, 0xF, 0xF, false));
+}
+
+// runtime-valued shift that folds to one of the immediates once the caller's
+// loops are unrolled
+__device__ __forceinline__ uint2 shift_rows_n(uint2 v, int sh)
+{
+    switch (sh) {
+    case 1: return shift_rows<1>(v);
+    case 2: return shift_rows<2>(v);
+    case 3: return shift_rows<3>(v);
+    case 4: return shift_rows<4>(v);
+    case 5: return shift_rows<5>(v);
+    case 6: return shift_rows<6>(v);
+    case 7: return shift_rows<7>(v);
+    case 8: return shift_rows<8>(v);
+    case 9: return shift_rows<9>(v);
+    case 10: return shift_rows<10>(v);
+    case 11: return shift_rows<11>(v);
+    case 12: return shift_rows<12>(v);
+    case 13: return shift_rows<13>(v);
+    case 14: return shift_rows<14>(v);
+    case 15: return shift_rows<15>(v);
+    default: return v;
+    }
+}
+
+// Accumulate half a k-tile (scale blocks 4H..4H+3); xa(b) gives block b's
+// A operand.  Working in halves keeps the live MFMA results small.
+template <int ROWS, int H, typename XA>
+__device__ __forceinline__ void gemv_half(const uint4 &cw, const uint2 &sw, XA &&xa, floatx4_t &acc)
+{
+    const uint32_t w0 = H ? cw.z : cw.x;
+    const uint32_t w1 = H ? cw.w : cw.y;
+    const uint32_t sv = H ? sw.y : sw.x;
     const floatx4_t zero = {0.f, 0.f, 0.f, 0.f};
-    floatx4_t p[8];
+    floatx4_t p[4];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const uint32_t w = words[b >> 1];
+    for (int bb = 0; bb < 4; ++bb) {
+        const uint32_t w = (bb < 2) ? w0 : w1;
         uint32_t lo, hi;
-        if (b & 1) {
+        if (bb & 1) {
             lo = fp4x2_to_bf16x2<2>(w);
             hi = fp4x2_to_bf16x2<3>(w);
         } else {
             lo = fp4x2_to_bf16x2<0>(w);
             hi = fp4x2_to_bf16x2<1>(w);
         }
-        const uint2 bq = make_uint2(lo, hi);
-        const short4_t a = __builtin_bit_cast(short4_t, xw[b]);
-        const short4_t bb = __builtin_bit_cast(short4_t, bq);
-        p[b] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bb, zero, 0, 0, 0);
+        const short4_t a = __builtin_bit_cast(short4_t, xa(4 * H + bb));
+        const short4_t bq = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
+        p[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bq, zero, 0, 0, 0);
     }
 #pragma unroll
-    for (int b = 0; b < 8; ++b) {
+    for (int bb = 0; bb < 4; ++bb) {
         float s;
-        const uint32_t sv = (b < 4) ? sw.x : sw.y;
-        switch (b & 3) {
+        switch (bb) {
         case 0: s = e4m3_to_f32<0>(sv); break;
         case 1: s = e4m3_to_f32<1>(sv); break;
         case 2: s = e4m3_to_f32<2>(sv); break;
         default: s = e4m3_to_f32<3>(sv); break;
         }
 #pragma unroll
-        for (int i = 0; i < R; ++i)
-            acc[i] = __builtin_fmaf(s, p[b][i], acc[i]);
+        for (int i = 0; i < ROWS; ++i)
+            acc[i] = __builtin_fmaf(s, p[bb][i], acc[i]);
     }
 }
 
-template <int R>
-__global__ void __launch_bounds__(64 * kMaxSplit)
+template <int MT, bool XLDS>
+__global__ void __launch_bounds__(64 * kMaxWaves)
 gemv_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales, float g,
             const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K, int KT,
-            int S)
+            int NT, int TB, int S)
 {
-    const int t = blockIdx.x;
-    const int w = threadIdx.x >> 6;
+    using X = Shape<MT, XLDS>;
+    constexpr int PF = X::kPrefetch;
+    constexpr int PAIRS = X::kPairs;
+    constexpr int BPP = X::kBpp;
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
-    const int r = lane & 15;       // weight row within the tile / activation row
-    const int gq = lane >> 4;      // k-group within each scale block
-    const int c0 = (int)(((int64_t)KT * w) / S);
-    const int c1 = (int)(((int64_t)KT * (w + 1)) / S);
+    const int r = lane & 15;          // weight row in the tile / A-operand row
+    const int gq = lane >> 4;         // k-group within each scale block
+    const int tb = wave / S;
+    const int ks = wave - tb * S;
+    const int t = blockIdx.x * TB + tb;
+    const bool live = t < NT;
+    const int c0 = (int)(((int64_t)KT * ks) / S);
+    const int c1 = (int)(((int64_t)KT * (ks + 1)) / S);
+    const int n = live ? c1 - c0 : 0;
+    const int last = n > 0 ? n - 1 : 0;
 
-    const uint4 *pc = pcodes + (int64_t)t * KT * 64 + lane;
-    const uint2 *ps = pscales + (int64_t)t * KT * 16 + r;
-    const bool xrow = r < M;
-    const uint16_t *xr = x + (int64_t)(xrow ? r : 0) * K + 4 * gq;
+    const int xbytes = XLDS ? M * KT * 256 : 0;
+    uint8_t *xl = smem;
+    uint8_t *zstrip = smem + xbytes;
+    floatx4_t *red = reinterpret_cast<floatx4_t *>(smem + xbytes + (XLDS ? kZeroBytes : 0));
 
-    uint4 cw[kPrefetch];
-    uint2 sw[kPrefetch];
-    uint2 xw[kPrefetch][8];
+    const uint4 *pc = pcodes + ((int64_t)(live ? t : 0) * KT + c0) * 64 + lane;
+    const uint2 *ps = pscales + ((int64_t)(live ? t : 0) * KT + c0) * 16 + r;
 
-    auto load = [&](int slot, int c) {
-        cw[slot] = load_stream16(pc + (int64_t)c * 64);
-        sw[slot] = ps[(int64_t)c * 16];
+    // ---- activation pieces riding in the ring (!XLDS) ----
+    // This lane's piece in pair j of k-tile c: row xm, block j*BPP + xt,
+    // k = 128c + 16(j*BPP + xt) + 4gq.  Lanes past the packed pieces repeat
+    // the last one (their A rows are discarded).
+    const int mm = MT == 0 ? 16 : MT;
+    int xm = MT == 0 ? r : r % mm;
+    int xt = MT == 0 ? 0 : r / mm;
+    if (xt > BPP - 1)
+        xt = BPP - 1;
+    if (xm > M - 1)
+        xm = M - 1;
+    const int xk = 16 * xt + 4 * gq;
+    const uint16_t *xrowg = x + (int64_t)xm * K;
+
+    // 1. issue this wave's activation staging loads.  With split-K (S > 1)
+    //    each wave stages exactly the k-tiles it will read, so no workgroup
+    //    barrier stands between a wave and its first tile; with several row
+    //    tiles per workgroup (TB > 1) the waves share one copy of all K,
+    //    staged in TB parts behind a barrier.
+    const int sc0 = TB > 1 ? (int)(((int64_t)KT * tb) / TB) : c0;
+    const int sn = TB > 1 ? (int)(((int64_t)KT * (tb + 1)) / TB) - sc0 : n;
+    const int gpr = sn * 32;                   // 8-byte groups per activation row
+    const int wn = gpr * M;                    // groups staged by this wave
+    // group lane + 64*j of this wave is (row, q): walk rows without dividing
+    int srow[kXStage], sq[kXStage];
+    if (XLDS) {
+        int row = 0, q = lane;
 #pragma unroll
-        for (int b = 0; b < 8; ++b) {
-            const int k = c * kTileK + 16 * b;          // + 4*gq folded into xr
-            xw[slot][b] = (xrow && k + 4 * gq < K)
-                              ? *reinterpret_cast<const uint2 *>(xr + k)
-                              : make_uint2(0u, 0u);
+        for (int j = 0; j < kXStage; ++j) {
+            while (q >= gpr && row < M) {
+                q -= gpr;
+                ++row;
+            }
+            srow[j] = row;
+            sq[j] = q;
+            q += 64;
+        }
+    }
+    uint2 xv[kXStage];
+    if (XLDS) {
+#pragma unroll
+        for (int j = 0; j < kXStage; ++j) {
+            const int k = 128 * sc0 + 4 * sq[j];
+            xv[j] = make_uint2(0u, 0u);
+            if (srow[j] < M && k < K)
+                xv[j] = *reinterpret_cast<const uint2 *>(x + (int64_t)srow[j] * K + k);
+        }
+    }
+
+    // ---- weight ring (+ activation pieces when !XLDS) ----
+    uint4 cw[PF];
+    uint2 sw[PF];
+    uint2 xq[PF][X::kRing];
+    // Reloads past the end of the range re-read the wave's last tile: the
+    // load stays unconditional (a conditional reload makes each ring slot a
+    // phi, resolved with copies that wait for every load in flight) and it
+    // hits lines this wave is fetching anyway.
+    auto load = [&](int u, int idx) {
+        const int j = idx < n ? idx : last;
+        cw[u] = load_stream16(pc + (int64_t)j * 64);
+        sw[u] = ps[(int64_t)j * 16];
+        if (!XLDS) {
+            const int kc = 128 * (c0 + j) + xk;
+#pragma unroll
+            for (int q = 0; q < PAIRS; ++q) {
+                const int k = kc + 16 * BPP * q;
+                xq[u][q] = *reinterpret_cast<const uint2 *>(xrowg + (k < K ? k : 0));
+            }
         }
     };
-
+    // prologue in slot order: the loop-entry state is merged into the loop's
+    // wait counts, so a reordered prologue would make every iteration wait
+    // for all loads in flight
 #pragma unroll
-    for (int u = 0; u < kPrefetch; ++u)
-        if (c0 + u < c1)
-            load(u, c0 + u);
+    for (int u = 0; u < PF; ++u) {
+        load(u, u);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 3. write the activations to LDS, permuted so that lane (r, gq) finds its
+    //    32 values of k-tile c at xl + ((r*KT + c)*4 + gq)*64
+    if (XLDS) {
+        auto put = [&](int row, int q, uint2 v) {
+            const int c = sc0 + (q >> 5), qq = q & 31;
+            *reinterpret_cast<uint2 *>(xl + ((row * KT + c) * 4 + (qq & 3)) * 64 + (qq >> 2) * 8) = v;
+        };
+#pragma unroll
+        for (int j = 0; j < kXStage; ++j)
+            if (srow[j] < M)
+                put(srow[j], sq[j], xv[j]);
+        // groups beyond kXStage per lane (long k-ranges or many rows)
+        if (wn > 64 * kXStage) {
+            int row = srow[kXStage - 1], q = sq[kXStage - 1] + 64;
+            for (;;) {
+                while (q >= gpr && row < M) {
+                    q -= gpr;
+                    ++row;
+                }
+                if (row >= M)
+                    break;
+                const int k = 128 * sc0 + 4 * q;
+                put(row, q, k < K ? *reinterpret_cast<const uint2 *>(x + (int64_t)row * K + k)
+                                  : make_uint2(0u, 0u));
+                q += 64;
+            }
+        }
+        if (lane < kZeroBytes / 4)
+            reinterpret_cast<uint32_t *>(zstrip)[lane] = 0u;   // same zeros from every wave
+        if (TB > 1) {
+            __syncthreads();
+        } else {
+            // the wave reads back only its own writes: wait for them to land
+            __builtin_amdgcn_s_waitcnt(0xc07f);                  // lgkmcnt(0)
+            __builtin_amdgcn_wave_barrier();
+        }
+    }
+
+    const uint8_t *xls = (r < M) ? xl + (r * KT * 4 + gq) * 64 : zstrip;
+    const int xstep = (r < M) ? 256 : 0;
 
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-    for (int c = c0; c < c1; c += kPrefetch) {
+    auto tile = [&](int u, int idx) {
+        const int c = c0 + idx;
+        if (XLDS) {
+            const uint4 *src = reinterpret_cast<const uint4 *>(xls + c * xstep);
 #pragma unroll
-        for (int u = 0; u < kPrefetch; ++u) {
-            if (c + u < c1) {
-                gemv_tile<R>(cw[u], sw[u], xw[u], acc);
-                if (c + u + kPrefetch < c1)
-                    load(u, c + u + kPrefetch);
+            for (int h = 0; h < 2; ++h) {
+                uint2 xf[4];
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    const uint4 v = src[2 * h + j];
+                    xf[2 * j] = make_uint2(v.x, v.y);
+                    xf[2 * j + 1] = make_uint2(v.z, v.w);
+                }
+                auto xa = [&](int b) { return xf[b & 3]; };
+                if (h == 0)
+                    gemv_half<X::kRows, 0>(cw[u], sw[u], xa, acc);
+                else
+                    gemv_half<X::kRows, 1>(cw[u], sw[u], xa, acc);
             }
+        } else {
+            uint2 xv[X::kRing];
+#pragma unroll
+            for (int q = 0; q < PAIRS; ++q)
+                xv[q] = xq[u][q];
+            if (128 * c + 128 > K) {
+                // k-tile padding past K (K % 128 != 0): zero those activations
+#pragma unroll
+                for (int q = 0; q < PAIRS; ++q)
+                    if (128 * c + xk + 16 * BPP * q >= K)
+                        xv[q] = make_uint2(0u, 0u);
+            }
+            auto xa = [&](int b) { return shift_rows_n(xv[b / BPP], MT == 0 ? 0 : MT * (b % BPP)); };
+            gemv_half<X::kRows, 0>(cw[u], sw[u], xa, acc);
+            gemv_half<X::kRows, 1>(cw[u], sw[u], xa, acc);
+        }
+        // pin this tile's fma chain here; otherwise chains are sunk past
+        // later tiles' MFMAs, which then all stay live
+        asm volatile("" : "+v"(acc));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    for (int i = 0; i < n; i += PF) {
+#pragma unroll
+        for (int u = 0; u < PF; ++u) {
+            if (i + u < n)
+                tile(u, i + u);
+            load(u, i + u + PF);
+            __builtin_amdgcn_sched_barrier(0);
         }
     }
 
     if (S > 1) {
-        __shared__ floatx4_t red[kMaxSplit][64];
-        red[w][lane] = acc;
+        red[wave * 64 + lane] = acc;
         __syncthreads();
-        if (w == 0) {
-            acc = red[0][lane];
+        if (ks == 0) {
+            acc = red[(tb * S) * 64 + lane];
             for (int v = 1; v < S; ++v)
-                acc += red[v][lane];
+                acc += red[(tb * S + v) * 64 + lane];
         }
     }
-    if (w == 0) {
+    if (ks == 0 && live) {
         // lane (r, gq) holds outputs y[4*gq + i][16*t + r], i = 0..3
-        const int n = 16 * t + r;
-        if (n < N) {
+        const int col = 16 * t + r;
+        if (col < N) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int m = 4 * gq + i;
+            for (int j = 0; j < 4; ++j) {
+                const int m = 4 * gq + j;
                 if (m < M)
-                    y[(int64_t)m * N + n] = g * acc[i];
+                    y[(int64_t)m * N + col] = g * acc[j];
             }
         }
     }
 }
 
-// k-splits per row tile: enough waves to cover the chip several times over,
-// at least 4 k-tiles per wave, at most kMaxSplit waves per workgroup.
-int choose_split(int64_t NT, int64_t KT)
+typedef void (*gemv_fn)(const uint4 *, const uint2 *, float, const uint16_t *, float *, int, int,
+                        int, int, int, int, int);
+
+template <bool XLDS>
+gemv_fn pick_kernel_x(int64_t M)
 {
-    const int64_t target_waves = 4096;
-    int64_t s = (target_waves + NT - 1) / NT;
-    if (s > KT / 4)
-        s = KT / 4;
-    if (s > kMaxSplit)
-        s = kMaxSplit;
-    if (s < 1)
-        s = 1;
-    return (int)s;
+    switch (M) {
+    case 1: return gemv_kernel<1, XLDS>;
+    case 2: return gemv_kernel<2, XLDS>;
+    case 3: return gemv_kernel<3, XLDS>;
+    case 4: return gemv_kernel<4, XLDS>;
+    case 5: return gemv_kernel<5, XLDS>;
+    case 6: return gemv_kernel<6, XLDS>;
+    case 7: return gemv_kernel<7, XLDS>;
+    case 8: return gemv_kernel<8, XLDS>;
+    default: return gemv_kernel<0, XLDS>;
+    }
+}
+
+gemv_fn pick_kernel(int64_t M, bool xlds)
+{
+    return xlds ? pick_kernel_x<true>(M) : pick_kernel_x<false>(M);
+}
+
+struct Plan {
+    gemv_fn fn;
+    int TB, S;
+    size_t lds;
+    int64_t blocks;
+};
+
+int device_cus()
+{
+    static int cus[64] = {0};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64)
+        return 256;
+    if (cus[dev] == 0) {
+        int v = 0;
+        if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            v <= 0)
+            v = 256;
+        cus[dev] = v;
+    }
+    return cus[dev];
+}
+
+// Launch shape: among (TB, S) with TB = 1 for S > 1 (at least 2 k-tiles per
+// wave), the one with the most waves whose workgroups are all resident at
+// once (one round, no tail); if none fits in one round, one wave per tile
+// (TB = 4 tiles per workgroup, sharing one staged copy of the activations).
+Plan make_plan(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t NT = n_tiles(N), KT = k_tiles(K);
+    const int64_t xbytes = M * KT * 256;
+    const bool xlds = xbytes <= kXLdsMaxBytes;
+    const size_t xl = xlds ? (size_t)xbytes + kZeroBytes : 0;
+    gemv_fn fn = pick_kernel(M, xlds);
+    const int cus = device_cus();
+    Plan best = {fn, 4, 1, xl, (NT + 3) / 4};
+    int64_t best_waves = 0;
+    auto consider = [&](int TB, int S) {
+        const size_t lds = xl + (S > 1 ? (size_t)TB * S * 1024 : 0);
+        int occ = 0;
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, reinterpret_cast<const void *>(fn),
+                                                         64 * TB * S, lds) != hipSuccess)
+            return;
+        const int64_t blocks = (NT + TB - 1) / TB;
+        if (occ <= 0 || blocks > (int64_t)cus * occ)
+            return;
+        const int64_t waves = blocks * TB * S;
+        if (waves > best_waves) {
+            best_waves = waves;
+            best = {fn, TB, S, lds, blocks};
+        }
+    };
+    for (int S = 2; S <= kMaxWaves; ++S)
+        if (KT / S >= 2)
+            consider(1, S);
+    for (int TB : {1, 2, 4})
+        consider(TB, 1);
+    return best;
+}
+
+struct CachedPlan {
+    int dev;
+    int64_t M, N, K;
+    Plan plan;
+};
+
+// Plans depend only on (device, M, N, K); a decode loop reuses a handful.
+Plan cached_plan(int64_t M, int64_t N, int64_t K)
+{
+    static std::mutex mu;
+    static std::vector<CachedPlan> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lock(mu);
+    for (const CachedPlan &c : cache)
+        if (c.dev == dev && c.M == M && c.N == N && c.K == K)
+            return c.plan;
+    const Plan p = make_plan(M, N, K);
+    if (cache.size() >= 256)
+        cache.clear();
+    cache.push_back({dev, M, N, K, p});
+    return p;
 }
 
 }  // namespace
@@ -167,19 +474,11 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream)
 {
-    const int64_t NT = n_tiles(N);
-    const int64_t KT = k_tiles(K);
-    const int S = choose_split(NT, KT);
-    const dim3 grid((unsigned)NT), block(64 * S);
-    const uint4 *pc = reinterpret_cast<const uint4 *>(packed_codes);
-    const uint2 *ps = reinterpret_cast<const uint2 *>(packed_scales);
-    const int m = (int)M, n = (int)N, k = (int)K, kt = (int)KT;
-    switch (M < 4 ? M : 4) {
-    case 1: hipLaunchKernelGGL(gemv_kernel<1>, grid, block, 0, stream, pc, ps, g, x, y, m, n, k, kt, S); break;
-    case 2: hipLaunchKernelGGL(gemv_kernel<2>, grid, block, 0, stream, pc, ps, g, x, y, m, n, k, kt, S); break;
-    case 3: hipLaunchKernelGGL(gemv_kernel<3>, grid, block, 0, stream, pc, ps, g, x, y, m, n, k, kt, S); break;
-    default: hipLaunchKernelGGL(gemv_kernel<4>, grid, block, 0, stream, pc, ps, g, x, y, m, n, k, kt, S); break;
-    }
+    const Plan p = cached_plan(M, N, K);
+    hipLaunchKernelGGL(p.fn, dim3((unsigned)p.blocks), dim3(64 * p.TB * p.S), p.lds, stream,
+                       reinterpret_cast<const uint4 *>(packed_codes),
+                       reinterpret_cast<const uint2 *>(packed_scales), g, x, y, (int)M, (int)N,
+                       (int)K, (int)k_tiles(K), (int)n_tiles(N), p.TB, p.S);
     return hipGetLastError();
 }
 
