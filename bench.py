@@ -11,7 +11,8 @@ through >= 512 MB of copies, so the 256 MB Infinity Cache cannot serve them.
 
 Also measured and reported in the same JSON line:
   roofline      the GEMV kernel: bytes per launch / mean launch duration (HIP
-                events around every launch on the launch stream) vs 8 TB/s;
+                events on the launch stream around the timed region, whose
+                launches are all this kernel) vs 8 TB/s;
                 `traffic` from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary in
                 profiles/ when it was taken on the current kernel source.
   prefill_gemm  the M = 512 prefill chunk (qkv 5120->14336, gate/up
@@ -74,26 +75,23 @@ def head_start(torch, ms):
     torch.cuda._sleep(int(ms * 1e-3 * 2.4e9))
 
 
-class Timed:
-    """HIP events around every launch, on the stream the launch uses."""
-
-    def __init__(self, torch):
-        self.torch = torch
-        self.pairs = []
-
-    def __call__(self, tag, fn):
-        s = self.torch.cuda.Event(enable_timing=True)
-        e = self.torch.cuda.Event(enable_timing=True)
-        s.record()
+def timed_region(torch, launches, steps):
+    """HIP events on the launch stream (the current stream, which the binding
+    launches on) around `launches` run back to back behind a head start.
+    Returns (ms per step, host seconds spent enqueueing)."""
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    head_start(torch, 0.05 * len(launches) + 5)
+    h0 = time.perf_counter()
+    t0.record(stream)
+    for fn in launches:
         fn()
-        e.record()
-        self.pairs.append((tag, s, e))
-
-    def ms(self, tag):
-        return sum(s.elapsed_time(e) for t, s, e in self.pairs if t == tag)
-
-    def count(self, tag):
-        return sum(1 for t, _, _ in self.pairs if t == tag)
+    t1.record(stream)
+    host_s = time.perf_counter() - h0
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, host_s
 
 
 def main():
@@ -146,7 +144,6 @@ def main():
         return lambda: fn(pc, ps, u["g"], u["x"], u["y"], c.M, c.N, c.K)
 
     out = {"metric": METRIC}
-    timer = Timed(torch)
 
     # ---- decode step: gate/up + down GEMV at M = 1 -------------------------
     dec = synth.workload_cases("dec")
@@ -160,28 +157,15 @@ def main():
             for u in dec_u:
                 launcher("gemv", u, i)()
         torch.cuda.synchronize()
-        t0 = torch.cuda.Event(enable_timing=True)
-        t1 = torch.cuda.Event(enable_timing=True)
         wall0 = time.perf_counter()
-        head_start(torch, 0.1 * args.steps + 5)
-        t0.record()
-        for i in range(args.steps):
-            for u in dec_u:
-                launcher("gemv", u, args.warmup + i)()
-        t1.record()
-        host_s = time.perf_counter() - wall0
-        torch.cuda.synchronize()
+        step_ms, host_s = timed_region(
+            torch, [launcher("gemv", u, args.warmup + i) for i in range(args.steps) for u in dec_u],
+            args.steps)
         wall = time.perf_counter() - wall0
-        step_ms = t0.elapsed_time(t1) / args.steps
-        # roofline pass: the same launches, each bracketed by HIP events on the
-        # launch stream, to get the kernel's mean duration per launch
-        head_start(torch, 0.1 * args.steps + 5)
-        for i in range(args.steps):
-            for u in dec_u:
-                timer("gemv", launcher("gemv", u, i))
-        torch.cuda.synchronize()
-        gemv_launches = timer.count("gemv")
-        gemv_ms = timer.ms("gemv") / gemv_launches
+        # every launch in the timed region is the decode GEMV kernel, so its
+        # mean duration per launch is the region's time over the launch count
+        # (launch gaps included, which only lowers the figure)
+        gemv_ms = step_ms / len(dec_u)
         launch_bytes = step_bytes / len(dec_u)
         achieved = launch_bytes / (gemv_ms * 1e-3) / 1e9
         digest = src_digest("q4p_gemv.hip")
@@ -200,7 +184,7 @@ def main():
                            u["w"][0][0].numel() + u["w"][0][1].numel() for u in dec_u)},
             "tokens_per_s": round(1.0 / (step_ms * 1e-3), 1),
             "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-            "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1>",
+            "roofline": {"bound": "hbm", "kernel": "gemv_kernel<1, true>",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "mean_launch_us": round(gemv_ms * 1e3, 3),
@@ -223,16 +207,11 @@ def main():
                 launcher("gemm", u, i)()
         torch.cuda.synchronize()
         gsteps = max(10, args.steps // 4)
-        head_start(torch, 0.1 * gsteps + 5)
-        for i in range(gsteps):
-            for u in pre_u:
-                timer("gemm_" + u["case"].name, launcher("gemm", u, i))
-        torch.cuda.synchronize()
         per = {}
         tot_flop = tot_ms = 0.0
         for u in pre_u:
             c = u["case"]
-            ms = timer.ms("gemm_" + c.name) / gsteps
+            ms, _ = timed_region(torch, [launcher("gemm", u, i) for i in range(gsteps)], gsteps)
             flop = 2.0 * c.M * c.N * c.K
             tot_flop += flop
             tot_ms += ms
@@ -261,11 +240,7 @@ def main():
                 n = max(10, args.steps // 4)
                 for i in range(3):
                     launcher("gemv", u, i)()
-                head_start(torch, 0.1 * n + 5)
-                for i in range(n):
-                    timer(f"{wl}_{c.name}", launcher("gemv", u, i))
-                torch.cuda.synchronize()
-                ms = timer.ms(f"{wl}_{c.name}") / n
+                ms, _ = timed_region(torch, [launcher("gemv", u, i) for i in range(n)], n)
                 shapes[f"{wl}/{c.name}"] = {"M": c.M, "N": c.N, "K": c.K,
                                             "us": round(ms * 1e3, 2),
                                             "gbs": round(b / (ms * 1e-3) / 1e9, 1),
@@ -280,11 +255,8 @@ def main():
         ps = torch.empty(q4.q4proj_packed_scales_bytes(lm.N, lm.K), dtype=torch.uint8, device=dev)
         for i in range(2):
             q4.q4proj_pack(codes, scales, lm.N, lm.K, pc, ps)
-        head_start(torch, 5)
-        for i in range(5):
-            timer("pack", lambda: q4.q4proj_pack(codes, scales, lm.N, lm.K, pc, ps))
-        torch.cuda.synchronize()
-        ms = timer.ms("pack") / 5
+        ms, _ = timed_region(
+            torch, [lambda: q4.q4proj_pack(codes, scales, lm.N, lm.K, pc, ps)] * 5, 5)
         moved = codes.numel() + scales.numel() + pc.numel() + ps.numel()
         out["pack"] = {"N": lm.N, "K": lm.K, "us": round(ms * 1e3, 1),
                        "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
