@@ -71,10 +71,16 @@ size_t q4proj_packed_codes_bytes(int64_t N, int64_t K);
 size_t q4proj_packed_scales_bytes(int64_t N, int64_t K);
 
 /*
- * Device scratch a projection needs for (M, N, K).  Every kernel of this
- * library reduces in registers and LDS, so this is 0 for every valid shape;
- * workspace may then be NULL.  The arguments stay in the projection entry
- * points so that a future split-K kernel can use them without an ABI change.
+ * Device scratch q4proj_gemv needs for (M, N, K): 512 KiB for 1 <= M <= 16
+ * (valid N, K), 0 otherwise; q4proj_gemm needs none and ignores its workspace.
+ * The gemv workspace holds one 64-bit exchange word per output of the row
+ * tiles that two workgroups share.  Ownership and state:
+ *   - owned by the caller, 8-byte aligned, not overlapping any other argument;
+ *   - zero-filled by the caller before its first use; every call that
+ *     completes leaves it zero-filled again, so it is reused as is;
+ *   - calls that may run at the same time (different streams) need separate
+ *     workspaces; a call that faults or is aborted can leave it dirty, after
+ *     which it must be zero-filled again.
  */
 size_t q4proj_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -108,8 +114,12 @@ q4proj_status q4proj_unpack(const uint8_t *packed_codes, const uint8_t *packed_s
  * applied once per output after accumulation.  Deterministic: the same inputs
  * give the same bits on every call.
  * x must be 16-byte aligned (K % 16 == 0 keeps every row aligned).
- * Errors: EINVAL (null pointer, M/N/K <= 0, K % 16 != 0, misaligned x),
- *         EUNSUPPORTED (M > 16), EWORKSPACE, EDEVICE, EHIP.
+ * workspace: q4proj_workspace_bytes(M, N, K) bytes, zero-filled before first
+ * use (see above); NULL only when that size is 0.
+ * Errors: EINVAL (null pointer, M/N/K <= 0, K % 16 != 0, misaligned x or
+ *         workspace, workspace overlapping an argument),
+ *         EUNSUPPORTED (M > 16), EWORKSPACE (workspace_bytes too small),
+ *         EDEVICE, EHIP.
  */
 q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales,
                           float global_scale, const uint16_t *x, float *y, int64_t M,
@@ -122,7 +132,8 @@ q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_sca
  * tiles to bf16 (exactly: q*s has at most 6 significant bits) and runs bf16
  * matrix-core instructions with fp32 accumulation; g is applied once per
  * output after accumulation.  Deterministic.
- * Errors: EINVAL, EWORKSPACE, EDEVICE, EHIP.
+ * workspace is not used (may be NULL with workspace_bytes 0).
+ * Errors: EINVAL, EDEVICE, EHIP.
  */
 q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
                           float global_scale, const uint16_t *x, float *y, int64_t M,

@@ -137,6 +137,24 @@ def q4proj_unpack(packed_codes: torch.Tensor, packed_scales: torch.Tensor, N: in
                "q4proj_unpack")
 
 
+_workspaces: dict = {}
+
+
+def default_workspace(device, nbytes: int):
+    """A zero-filled device buffer of at least nbytes, one per device, reused by
+    every call that passes no workspace (calls leave it zero-filled).  Calls
+    that may run concurrently on one device need workspaces of their own."""
+    if nbytes <= 0:
+        return None
+    key = torch.device(device).index if torch.device(device).index is not None else \
+        torch.cuda.current_device()
+    ws = _workspaces.get(key)
+    if ws is None or ws.numel() < nbytes:
+        ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", key))
+        _workspaces[key] = ws
+    return ws
+
+
 def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, workspace, stream):
     dev = x.device
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
@@ -148,6 +166,8 @@ def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, w
     _need(x, "x", x.dtype, M * K, dev)
     _need(y, "y", torch.float32, M * N, dev)
     ws_ptr, ws_bytes = None, 0
+    if workspace is None and fn is _lib.q4proj_gemv:
+        workspace = default_workspace(dev, q4proj_workspace_bytes(M, N, K))
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()

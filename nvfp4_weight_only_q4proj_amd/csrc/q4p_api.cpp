@@ -68,7 +68,7 @@ bool overlap(const void *a, size_t na, const void *b, size_t nb)
 
 q4proj_status check_projection(const uint8_t *pc, const uint8_t *ps, const uint16_t *x,
                                const float *y, int64_t M, int64_t N, int64_t K,
-                               size_t workspace_bytes)
+                               size_t workspace_bytes, size_t workspace_need)
 {
     if (!pc || !ps || !x || !y)
         return Q4P_EINVAL;
@@ -83,7 +83,7 @@ q4proj_status check_projection(const uint8_t *pc, const uint8_t *ps, const uint1
         overlap(y, ybytes, pc, q4proj_packed_codes_bytes(N, K)) ||
         overlap(y, ybytes, ps, q4proj_packed_scales_bytes(N, K)))
         return Q4P_EINVAL;
-    if (workspace_bytes < q4proj_workspace_bytes(M, N, K))
+    if (workspace_bytes < workspace_need)
         return Q4P_EWORKSPACE;
     return Q4P_OK;
 }
@@ -108,10 +108,9 @@ size_t q4proj_packed_scales_bytes(int64_t N, int64_t K)
 
 size_t q4proj_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    (void)M;
-    (void)N;
-    (void)K;
-    return 0;
+    if (M <= 0 || M > Q4PROJ_GEMV_MAX_M || !shape_ok(N, K))
+        return 0;
+    return q4p::gemv_workspace_bytes(M, N, K);
 }
 
 q4proj_status q4proj_pack(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
@@ -158,18 +157,25 @@ q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_sca
                           float global_scale, const uint16_t *x, float *y, int64_t M, int64_t N,
                           int64_t K, void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)workspace;
+    const size_t need = q4proj_workspace_bytes(M, N, K);
     q4proj_status st = check_projection(packed_codes, packed_scales, x, y, M, N, K,
-                                        workspace_bytes);
+                                        workspace_bytes, need);
     if (st != Q4P_OK)
         return st;
     if (M > Q4PROJ_GEMV_MAX_M)
         return Q4P_EUNSUPPORTED;
+    if (need > 0 && (!workspace || !aligned(workspace, 8)))
+        return Q4P_EINVAL;
+    if (need > 0 && (overlap(workspace, need, y, (size_t)M * (size_t)N * sizeof(float)) ||
+                     overlap(workspace, need, x, (size_t)M * (size_t)K * 2) ||
+                     overlap(workspace, need, packed_codes, q4proj_packed_codes_bytes(N, K)) ||
+                     overlap(workspace, need, packed_scales, q4proj_packed_scales_bytes(N, K))))
+        return Q4P_EINVAL;
     st = check_device();
     if (st != Q4P_OK)
         return st;
     return record_hip(q4p::launch_gemv(packed_codes, packed_scales, global_scale, x, y, M, N, K,
-                                       static_cast<hipStream_t>(stream)));
+                                       workspace, static_cast<hipStream_t>(stream)));
 }
 
 q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
@@ -178,7 +184,7 @@ q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_sca
 {
     (void)workspace;
     q4proj_status st = check_projection(packed_codes, packed_scales, x, y, M, N, K,
-                                        workspace_bytes);
+                                        workspace_bytes, 0);
     if (st != Q4P_OK)
         return st;
     st = check_device();

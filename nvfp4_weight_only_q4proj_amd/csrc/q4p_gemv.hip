@@ -360,6 +360,276 @@ gemv_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
     }
 }
 
+// ---------------------------------------------------------------------------
+// Stream-K variant, used whenever the activations fit in LDS.
+//
+// The k-tiles of all row tiles, in packed-memory order (row tile t, k-tile c
+// at unit t*KT + c), are dealt out in equal contiguous ranges: G workgroups,
+// one per CU (each asks for more than half the CU's LDS, so no two share a
+// CU), then WPG waves per workgroup.  Every CU streams the same number of
+// bytes.  With 8 waves per CU and 4 tiles in flight per wave the chip keeps
+// about 9 MB of requests queued, where HBM delivers best: deeper queues from
+// every wave at once, or fewer waves with deeper rings, measured slower.
+//
+// A wave flushes its accumulator at each row-tile boundary.  A row tile that
+// lies wholly inside one wave is stored directly.  Partial row tiles go to
+// LDS; after the stream the lowest contributing wave of the workgroup adds
+// the parts in wave order.  A row tile that also continues in the
+// neighbouring workgroup (ranges are at least KT units, so at most two
+// workgroups share one) is finished through a 64-bit exchange per output:
+// each side swaps (flag, partial) into a workspace word; the side that finds
+// the flag set adds the two partials -- fp32 addition of two values is
+// commutative, so the result does not depend on which side comes second --
+// stores y and clears the word for the next call.  No fences, no waiting.
+
+constexpr int kSkMaxGroups = 256;
+constexpr int kSkMaxWaves = 8;
+constexpr int kSkPrefetch = 4;
+constexpr int kSkXMaxBytes = 128 * 1024;       // + 16 KB of partial sums stays within 160 KB
+constexpr int kSkLdsFloor = 96 * 1024;
+constexpr int kSkStage = 8;                    // 16-byte activation loads per lane before the ring
+
+struct SkArgs {
+    int U;                                     // units = NT * KT (< 2^31)
+    int base, rem;                             // U / G, U % G
+    int M, N, K, KT, NT, G, WPG;
+    float g;
+};
+
+template <int ROWS, int PF>
+__global__ void __launch_bounds__(64 * kSkMaxWaves)
+gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
+               const uint16_t *__restrict__ x, float *__restrict__ y,
+               unsigned long long *__restrict__ xch, SkArgs a)
+{
+    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+    const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    const int lane = threadIdx.x & 63;
+    const int r = lane & 15;
+    const int gq = lane >> 4;
+    const int G = a.G, WPG = a.WPG, KT = a.KT, M = a.M, K = a.K;
+
+    // workgroups are dealt round-robin to the 8 XCDs: give consecutive ranges
+    // to workgroups on the same XCD
+    const int b = blockIdx.x;
+    const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+    // balanced split: the first `rem` groups (and, inside a group, the first
+    // `wr` waves) take one unit more
+    const int UW0 = L * a.base + (L < a.rem ? L : a.rem);
+    const int UWn = a.base + (L < a.rem ? 1 : 0);
+    const int UW1 = UW0 + UWn;
+    const int wb = UWn / WPG, wr = UWn - wb * WPG;
+    auto wave_start = [&](int v) { return UW0 + v * wb + (v < wr ? v : wr); };
+    // wave of this workgroup that holds unit u (UW0 <= u < UW1)
+    auto wave_of = [&](int u) {
+        const int o = u - UW0, big = wr * (wb + 1);
+        return o < big ? o / (wb + 1) : wr + (o - big) / wb;
+    };
+    const int u0 = wave_start(wave), u1 = wave_start(wave + 1);
+    const int n = u1 - u0;
+    const int ulast = n > 0 ? u1 - 1 : 0;
+
+    const int xbytes = M * KT * 256;
+    uint8_t *xl = smem;
+    uint8_t *zstrip = smem + xbytes;
+    floatx4_t *part = reinterpret_cast<floatx4_t *>(smem + xbytes + kZeroBytes);
+
+    // 1. activation staging loads (all of x: rows < M, every k-tile)
+    const int nthr = 64 * WPG;
+    const int gpr = KT * 16;                   // 16-byte groups per activation row
+    const int ngroups = M * gpr;
+    // group tid + i*nthr is (row srow[i], group sq[i] of that row): walk the
+    // rows instead of dividing
+    uint4 xs[kSkStage];
+    int srow[kSkStage], sq[kSkStage];
+    {
+        int row = 0, q = (int)threadIdx.x;
+#pragma unroll
+        for (int i = 0; i < kSkStage; ++i) {
+            while (q >= gpr && row < M) {
+                q -= gpr;
+                ++row;
+            }
+            srow[i] = row;
+            sq[i] = q;
+            q += nthr;
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < kSkStage; ++i) {
+        xs[i] = make_uint4(0u, 0u, 0u, 0u);
+        const int k = sq[i] * 8;
+        if (srow[i] < M && k < K)
+            xs[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)srow[i] * K + k);
+    }
+
+    // 2. weight ring prologue, in slot order
+    const uint4 *pc = pcodes + lane;
+    const uint2 *ps = pscales + r;
+    uint4 cw[PF];
+    uint2 sw[PF];
+    auto load = [&](int s, int u) {
+        const int j = u <= ulast ? u : ulast;
+        cw[s] = load_stream16(pc + (int64_t)j * 64);
+        sw[s] = ps[(int64_t)j * 16];
+    };
+#pragma unroll
+    for (int s = 0; s < PF; ++s) {
+        load(s, u0 + s);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+
+    // 3. activations to LDS: lane (r, gq) finds its 32 values of k-tile c at
+    //    xl + ((r*KT + c)*4 + gq)*64
+    auto put = [&](int m, int q, uint4 v) {
+        const int c = q >> 4, j = q & 15;
+        uint8_t *base = xl + ((m * KT + c) * 4 + ((2 * j) & 3)) * 64 + (j >> 1) * 8;
+        *reinterpret_cast<uint2 *>(base) = make_uint2(v.x, v.y);
+        *reinterpret_cast<uint2 *>(base + 64) = make_uint2(v.z, v.w);
+    };
+#pragma unroll
+    for (int i = 0; i < kSkStage; ++i)
+        if (srow[i] < M)
+            put(srow[i], sq[i], xs[i]);
+    if (ngroups > kSkStage * nthr) {
+        int row = srow[kSkStage - 1], q = sq[kSkStage - 1] + nthr;
+        for (;;) {
+            while (q >= gpr && row < M) {
+                q -= gpr;
+                ++row;
+            }
+            if (row >= M)
+                break;
+            const int k = q * 8;
+            put(row, q, k < K ? *reinterpret_cast<const uint4 *>(x + (int64_t)row * K + k)
+                              : make_uint4(0u, 0u, 0u, 0u));
+            q += nthr;
+        }
+    }
+    if (threadIdx.x < kZeroBytes / 4)
+        reinterpret_cast<uint32_t *>(zstrip)[threadIdx.x] = 0u;
+    __syncthreads();
+
+    // 4. stream this wave's units
+    const uint8_t *xls = (r < M) ? xl + (r * KT * 4 + gq) * 64 : zstrip;
+    const int xstep = (r < M) ? 256 : 0;
+    const float g = a.g;
+    const int N = a.N;
+    const int tfirst = n > 0 ? u0 / KT : 0;
+    const int cfirst = n > 0 ? u0 - tfirst * KT : 0;
+    int t = tfirst, c = cfirst;
+
+    auto store_y = [&](int tt, const floatx4_t &v) {
+        const int col = 16 * tt + r;
+        if (col < N) {
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j) {
+                const int m = 4 * gq + j;
+                if (m < M)
+                    y[(int64_t)m * N + col] = g * v[j];
+            }
+        }
+    };
+
+    floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
+    auto tile = [&](int s, int cc) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(xls + cc * xstep);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            uint2 xf[4];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const uint4 v = src[2 * h + j];
+                xf[2 * j] = make_uint2(v.x, v.y);
+                xf[2 * j + 1] = make_uint2(v.z, v.w);
+            }
+            auto xa = [&](int bb) { return xf[bb & 3]; };
+            if (h == 0)
+                gemv_half<ROWS, 0>(cw[s], sw[s], xa, acc);
+            else
+                gemv_half<ROWS, 1>(cw[s], sw[s], xa, acc);
+        }
+        asm volatile("" : "+v"(acc));
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    for (int i = 0; i < n; i += PF) {
+#pragma unroll
+        for (int s = 0; s < PF; ++s) {
+            if (i + s < n) {
+                tile(s, c);
+                ++c;
+                if (c == KT || i + s == n - 1) {
+                    const int cstart = (t == tfirst) ? cfirst : 0;
+                    if (cstart == 0 && c == KT)
+                        store_y(t, acc);                           // whole row tile
+                    else
+                        part[(wave * 2 + (t == tfirst ? 0 : 1)) * 64 + lane] = acc;
+                    acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                    if (c == KT) {
+                        c = 0;
+                        ++t;
+                    }
+                }
+            }
+            load(s, u0 + i + s + PF);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+
+    // 5. finish the row tiles split between waves or workgroups
+    __syncthreads();
+    if (n == 0)
+        return;
+    const int tlast = (u1 - 1) / KT;
+    for (int side = 0; side < 2; ++side) {
+        const int tau = side == 0 ? tfirst : tlast;
+        if (side == 1 && tlast == tfirst)
+            break;
+        const int ta = tau * KT, tb = ta + KT;
+        const int a0 = ta > UW0 ? ta : UW0, a1 = tb < UW1 ? tb : UW1;
+        const int vlo = wave_of(a0), vhi = wave_of(a1 - 1);
+        const bool cross = ta < UW0 || tb > UW1;
+        if (vlo != wave || (vlo == vhi && !cross))
+            continue;                                   // another wave's, or stored already
+        floatx4_t sum = {0.f, 0.f, 0.f, 0.f};
+        for (int v = vlo; v <= vhi; ++v) {
+            const int vfirst = wave_start(v) / KT;
+            const floatx4_t pv = part[(v * 2 + (tau == vfirst ? 0 : 1)) * 64 + lane];
+            if (v == vlo)
+                sum = pv;
+            else
+                sum += pv;
+        }
+        if (!cross) {
+            store_y(tau, sum);
+            continue;
+        }
+        const int bnd = ta < UW0 ? L - 1 : L;           // boundary between groups bnd, bnd + 1
+        unsigned long long *slot = xch + ((int64_t)bnd * 64 + lane) * 4;
+        const int col = 16 * tau + r;
+#pragma unroll
+        for (int j = 0; j < ROWS; ++j) {
+            const int m = 4 * gq + j;
+            if (m < M) {
+                // copy the element out first: clang mis-lowers a bit_cast whose
+                // operand is a vector element (it reads element 0)
+                const float sj = sum[j];
+                const unsigned long long mine =
+                    (1ull << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, sj);
+                const unsigned long long old = __hip_atomic_exchange(
+                    slot + j, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                if (old >> 32) {
+                    const float other = __builtin_bit_cast(float, (uint32_t)old);
+                    if (col < N)
+                        y[(int64_t)m * N + col] = g * (other + sj);
+                    __hip_atomic_store(slot + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+            }
+        }
+    }
+}
+
 typedef void (*gemv_fn)(const uint4 *, const uint2 *, float, const uint16_t *, float *, int, int,
                         int, int, int, int, int);
 
@@ -468,17 +738,104 @@ Plan cached_plan(int64_t M, int64_t N, int64_t K)
     return p;
 }
 
+typedef void (*gemv_sk_fn)(const uint4 *, const uint2 *, const uint16_t *, float *,
+                           unsigned long long *, SkArgs);
+
+gemv_sk_fn pick_sk_kernel(int64_t M)
+{
+    switch (M) {
+    case 1: return gemv_sk_kernel<1, kSkPrefetch>;
+    case 2: return gemv_sk_kernel<2, kSkPrefetch>;
+    case 3: return gemv_sk_kernel<3, kSkPrefetch>;
+    default: return gemv_sk_kernel<4, kSkPrefetch>;
+    }
+}
+
+struct SkPlan {
+    gemv_sk_fn fn;
+    SkArgs args;
+    size_t lds;
+};
+
+// One workgroup per CU (at most kSkMaxGroups), but no more workgroups than
+// row tiles, so that every workgroup's range covers at least KT units and a
+// row tile is shared by at most two workgroups.
+SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t KT = k_tiles(K), NT = n_tiles(N), U = NT * KT;   // U < 2^31 (checked by the caller)
+    int64_t G = device_cus();
+    if (G > kSkMaxGroups)
+        G = kSkMaxGroups;
+    if (G > NT)
+        G = NT;
+    int64_t WPG = kSkMaxWaves;
+    if (WPG > U / G)
+        WPG = U / G;
+    SkPlan p;
+    p.fn = pick_sk_kernel(M);
+    p.args = SkArgs{(int)U, (int)(U / G), (int)(U % G), (int)M, (int)N, (int)K, (int)KT, (int)NT,
+                    (int)G, (int)WPG, 0.f};
+    size_t lds = (size_t)(M * KT * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
+    if (lds < (size_t)kSkLdsFloor)
+        lds = kSkLdsFloor;
+    p.lds = lds;
+    return p;
+}
+
+struct CachedSkPlan {
+    int dev;
+    int64_t M, N, K;
+    SkPlan plan;
+};
+
+SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K)
+{
+    static std::mutex mu;
+    static std::vector<CachedSkPlan> cache;
+    int dev = 0;
+    (void)hipGetDevice(&dev);
+    std::lock_guard<std::mutex> lock(mu);
+    for (const CachedSkPlan &c : cache)
+        if (c.dev == dev && c.M == M && c.N == N && c.K == K)
+            return c.plan;
+    const SkPlan p = make_sk_plan(M, N, K);
+    if (cache.size() >= 256)
+        cache.clear();
+    cache.push_back({dev, M, N, K, p});
+    return p;
+}
+
 }  // namespace
+
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    (void)N;
+    (void)K;
+    if (M < 1 || M > 16)
+        return 0;
+    return (size_t)kSkMaxGroups * 64 * 4 * sizeof(unsigned long long);
+}
 
 hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream)
+                       void *workspace, hipStream_t stream)
 {
+    const int64_t KT = k_tiles(K), NT = n_tiles(N);
+    if (M * KT * 256 <= kSkXMaxBytes && NT * KT < ((int64_t)1 << 31)) {
+        const SkPlan p = cached_sk_plan(M, N, K);
+        SkArgs args = p.args;
+        args.g = g;
+        hipLaunchKernelGGL(p.fn, dim3((unsigned)args.G), dim3(64 * args.WPG), p.lds, stream,
+                           reinterpret_cast<const uint4 *>(packed_codes),
+                           reinterpret_cast<const uint2 *>(packed_scales), x, y,
+                           static_cast<unsigned long long *>(workspace), args);
+        return hipGetLastError();
+    }
     const Plan p = cached_plan(M, N, K);
     hipLaunchKernelGGL(p.fn, dim3((unsigned)p.blocks), dim3(64 * p.TB * p.S), p.lds, stream,
                        reinterpret_cast<const uint4 *>(packed_codes),
                        reinterpret_cast<const uint2 *>(packed_scales), g, x, y, (int)M, (int)N,
-                       (int)K, (int)k_tiles(K), (int)n_tiles(N), p.TB, p.S);
+                       (int)K, (int)KT, (int)NT, p.TB, p.S);
     return hipGetLastError();
 }
 

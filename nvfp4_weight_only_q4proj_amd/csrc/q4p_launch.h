@@ -14,9 +14,13 @@ hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, int64_t N, i
 hipError_t launch_unpack(const uint8_t *packed_codes, const uint8_t *packed_scales, int64_t N,
                          int64_t K, uint8_t *codes, uint8_t *scales, hipStream_t stream);
 
+// Device scratch q4proj_gemv needs (zero-filled before first use; each call
+// leaves it zero-filled again).
+size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
 hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream);
+                       void *workspace, hipStream_t stream);
 
 hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,

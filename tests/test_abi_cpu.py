@@ -46,7 +46,10 @@ def test_packed_sizes(q4, N, K):
     nt, kt = -(-N // 16), -(-K // 128)
     assert q4.q4proj_packed_codes_bytes(N, K) == nt * kt * 1024 >= N * K // 2
     assert q4.q4proj_packed_scales_bytes(N, K) == nt * kt * 128 >= N * K // 16
-    assert q4.q4proj_workspace_bytes(7, N, K) == 0
+    # gemv's exchange words: one 64-bit word x 4 rows x 64 lanes per workgroup boundary
+    assert q4.q4proj_workspace_bytes(1, N, K) == q4.q4proj_workspace_bytes(16, N, K) == 512 * 1024
+    assert q4.q4proj_workspace_bytes(17, N, K) == 0
+    assert q4.q4proj_workspace_bytes(512, N, K) == 0
 
 
 @pytest.mark.parametrize("N,K", [(0, 16), (16, 0), (16, 8), (16, 24), (-1, 16)])
@@ -57,10 +60,11 @@ def test_packed_sizes_invalid(q4, N, K):
 
 # Fake, well-aligned, non-overlapping addresses: every call below must be
 # rejected by the host-side checks before any HIP call is made.
-A, B, X, Y = 0x10000000, 0x20000000, 0x30000000, 0x40000000
+A, B, X, Y, W = 0x10000000, 0x20000000, 0x30000000, 0x40000000, 0x50000000
+WSB = 512 * 1024
 
 
-def proj(lib, fn, pc=A, ps=B, x=X, y=Y, M=1, N=64, K=256, ws=None, wsb=0):
+def proj(lib, fn, pc=A, ps=B, x=X, y=Y, M=1, N=64, K=256, ws=W, wsb=WSB):
     return getattr(lib, fn)(pc, ps, ctypes.c_float(1.0), x, y, M, N, K, ws, wsb, None)
 
 
@@ -81,6 +85,16 @@ def test_projection_validation(q4, fn):
     assert proj(lib, fn, y=Y + 2) == q4.EINVAL
     assert proj(lib, fn, y=X + 64) == q4.EINVAL      # y overlaps x
     assert proj(lib, fn, y=A) == q4.EINVAL           # y overlaps the packed codes
+
+
+def test_gemv_workspace_validation(q4):
+    lib = q4.library()
+    assert proj(lib, "q4proj_gemv", wsb=WSB - 8) == q4.EWORKSPACE
+    assert proj(lib, "q4proj_gemv", ws=None, wsb=0) == q4.EWORKSPACE
+    assert proj(lib, "q4proj_gemv", ws=None) == q4.EINVAL        # size given, no buffer
+    assert proj(lib, "q4proj_gemv", ws=W + 4) == q4.EINVAL       # 8-byte alignment
+    assert proj(lib, "q4proj_gemv", ws=Y - 4096) == q4.EINVAL    # overlaps y
+    assert proj(lib, "q4proj_gemv", ws=X) == q4.EINVAL           # overlaps x
 
 
 def test_gemv_m_range(q4):
@@ -115,4 +129,5 @@ def test_no_device_no_fallback(q4):
     lib = q4.library()
     assert proj(lib, "q4proj_gemv") == q4.EDEVICE
     assert proj(lib, "q4proj_gemm", M=512) == q4.EDEVICE
+    assert proj(lib, "q4proj_gemm", M=512, ws=None, wsb=0) == q4.EDEVICE   # gemm needs none
     assert lib.q4proj_pack(A, B, 16, 128, X, Y, None) == q4.EDEVICE
