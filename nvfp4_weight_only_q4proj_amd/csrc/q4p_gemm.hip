@@ -12,24 +12,28 @@
 //    partial sums are added through LDS at the end.  Two waves per SIMD let
 //    one wave's dequantisation and LDS waits overlap the other's MFMAs.
 //  * Each wave pair owns Q = T/4 whole weight tiles (all 128 rows) plus a
-//    quarter (32 rows) of each of the RT = T%4 remaining tiles, so all waves
-//    do exactly the same number of MFMAs whatever T is.
+//    share of the RT = T%4 remaining tiles: half of one tile (64 rows) when
+//    RT = 2, a quarter (32 rows) of each otherwise, so all waves do the same
+//    number of MFMAs whatever T is.  A wave walks the eight 16-row blocks of
+//    activations starting at its share of the remaining tiles, so those
+//    MFMAs reuse the activation operands it reads anyway.
 //  * Operands reach LDS without passing through registers: per k-tile (128 k)
 //    the 128 activation rows and the workgroup's T packed code tiles and
-//    scale tiles are fetched with 16-byte direct-to-LDS loads into one of
-//    three stages, two k-tiles ahead of the MFMAs.  Workgroup barriers are
-//    bare s_barrier with an explicit wait for the stage being consumed (a
-//    full barrier would also drain the loads of the stages in flight).
-//  * Activation rows are stored in LDS with the 16-byte chunks of each row
-//    XOR-swizzled by the row index, so that the sixteen rows an A-operand read
-//    touches fall in sixteen different bank groups.  A lane's eight bf16 for
-//    one 16x16x32 MFMA are two 8-byte pieces (k = 4g..4g+3 of two adjacent
-//    scale blocks), matching the k-values its weight code word holds.
-//  * Weights: each wave reads its tiles' 16-byte code slots and 8-byte scale
-//    rows from LDS and dequantises them to bf16 with the e4m3 scale folded in
-//    (exact: q*s has <= 6 significant bits).  One 32-bit code word = two
-//    scale blocks x 4 codes = one MFMA operand.
-//  * fp32 accumulation in the MFMA; y = g * acc stored once.
+//    scale tiles are fetched with 16-byte buffer loads straight into one of
+//    three LDS stages, two k-tiles ahead of the MFMAs.  Offsets past the end
+//    of a buffer read as zero, which covers rows past M and tiles past N.
+//    Workgroup barriers are bare s_barrier with an explicit wait for the
+//    stage being consumed (a full barrier would also drain the loads of the
+//    stages in flight).
+//  * MFMA k-order: in 16x16x32 step d, lane (r, gq) supplies k = 32d + 8gq
+//    + 0..7, i.e. one 16-byte chunk of an activation row (one ds_read_b128).
+//    Chunks are XOR-swizzled by row within LDS so the rows one read touches
+//    fall in different banks.  The matching eight weight codes are halves of
+//    two code slots of the packed tile (one byte permute); they share one
+//    e4m3 scale.
+//  * Dequantisation to bf16 with the e4m3 scale folded in is exact: q*s has
+//    at most 6 significant bits.  fp32 accumulation in the MFMA; y = g * acc
+//    stored once.
 #include "q4p_device.h"
 #include "q4p_launch.h"
 
@@ -41,50 +45,37 @@ constexpr int kBM = 128;                       // activation rows per workgroup
 constexpr int kMaxT = 17;                      // weight tiles per workgroup
 constexpr int kXStageBytes = kBM * 256;        // one k-tile of activations
 constexpr int kWStageBytes = kMaxT * (kTileCodeBytes + kTileScaleBytes);
+// A buffer offset at or past a buffer's size reads as zero; this one marks
+// rows and tiles outside the problem (it stays past every buffer after the
+// per-stage advance, since one launch addresses less than 1 GiB per buffer).
+constexpr uint32_t kOutside = 0x80000000u;
+constexpr int64_t kMaxLaunchBytes = int64_t(1) << 30;
+// Stage-load advance that lands every lane past the end of its buffer (a
+// load past the last k-tile then only writes zeros to a free stage).
+constexpr uint32_t kSkip = 0x40000000u;
 
-// One 16x16x32 MFMA operand from code word `wd` (blocks 2d and 2d+1 of the
-// lane's row) with their decoded scales s0, s1.
-__device__ __forceinline__ bf16x8_t dequant_operand(uint32_t wd, float s0, float s1)
+// Raw buffer resource over `bytes` bytes at p (gfx9 dword 3 for untyped
+// 32-bit-element access; offsets are checked against `bytes`).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
+}
+
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds, uint32_t voffset)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+}
+
+// Eight e2m1 codes (one dword, low nibble first) times one decoded scale.
+__device__ __forceinline__ bf16x8_t dequant8(uint32_t wd, float s)
 {
     uint4 v;
-    v.x = fp4x2_scaled_to_bf16x2<0>(wd, s0);
-    v.y = fp4x2_scaled_to_bf16x2<1>(wd, s0);
-    v.z = fp4x2_scaled_to_bf16x2<2>(wd, s1);
-    v.w = fp4x2_scaled_to_bf16x2<3>(wd, s1);
+    v.x = fp4x2_scaled_to_bf16x2<0>(wd, s);
+    v.y = fp4x2_scaled_to_bf16x2<1>(wd, s);
+    v.z = fp4x2_scaled_to_bf16x2<2>(wd, s);
+    v.w = fp4x2_scaled_to_bf16x2<3>(wd, s);
     return __builtin_bit_cast(bf16x8_t, v);
-}
-
-template <int D>
-__device__ __forceinline__ bf16x8_t weight_operand(const uint4 &c, const uint2 &s)
-{
-    const uint32_t wd = D == 0 ? c.x : D == 1 ? c.y : D == 2 ? c.z : c.w;
-    const uint32_t sv = D < 2 ? s.x : s.y;
-    float s0, s1;
-    if (D & 1) {
-        s0 = e4m3_to_f32<2>(sv);
-        s1 = e4m3_to_f32<3>(sv);
-    } else {
-        s0 = e4m3_to_f32<0>(sv);
-        s1 = e4m3_to_f32<1>(sv);
-    }
-    return dequant_operand(wd, s0, s1);
-}
-
-// Operand of the first (DD = 0) or second (DD = 1) of a wave's two k-steps,
-// from its two code words and the scale dword of their four blocks.
-template <int DD>
-__device__ __forceinline__ bf16x8_t weight_operand_half(const uint2 &c, uint32_t sv)
-{
-    const uint32_t wd = DD == 0 ? c.x : c.y;
-    float s0, s1;
-    if (DD == 1) {
-        s0 = e4m3_to_f32<2>(sv);
-        s1 = e4m3_to_f32<3>(sv);
-    } else {
-        s0 = e4m3_to_f32<0>(sv);
-        s1 = e4m3_to_f32<1>(sv);
-    }
-    return dequant_operand(wd, s0, s1);
 }
 
 // gfx9 s_waitcnt immediate: wait until at most n vector-memory operations of
@@ -104,11 +95,13 @@ __device__ __forceinline__ void wait_vm(int n)
 
 template <int Q, int RT>
 __global__ void __launch_bounds__(512)
-gemm_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales, float g,
-            const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int K, int KT,
-            int NT, int T)
+gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ pscales, float g,
+            const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int64_t ldy,
+            int K, int KT, int NT)
 {
     constexpr int TT = 4 * Q + RT;                         // tiles per workgroup (== T)
+    constexpr int RB = RT == 2 ? 1 : RT;                   // remaining-tile operands per wave
+    constexpr int RR = RT == 2 ? 4 : 2;                    // 16-row blocks per such operand
     // weight chunks (16 bytes) per stage: 64 per code tile + 8 per scale tile,
     // spread over whole 64-lane loads, the same number for every wave
     constexpr int kWChunks = 72 * TT;
@@ -129,85 +122,102 @@ gemm_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
     const int gq = lane >> 4;
     const int m0 = blockIdx.y * kBM;
     const int tile0 = blockIdx.x * TT;
-    (void)T;
+    // first 16-row block of this wave's share of the remaining tiles; the
+    // wave visits row blocks rb, rb+1, ... (mod 8)
+    const int rb = RT == 2 ? 4 * (w & 1) : 2 * w;
 
-    // ---- direct-to-LDS stage loads ---------------------------------------
-    // Activations: wave v, load i covers LDS slots 64*(4v+i) .. +63, i.e.
-    // rows 4*(4v+i) .. +3; lane l -> row 4*(4v+i) + l/16, slot position
-    // l%16, which holds chunk (l%16) ^ (row%16) of the row (8 bf16 each).
-    // Rows past M read row M-1 (outputs never stored); chunks past K read the
-    // row start and are zeroed after landing (ragged last k-tile only).
-    // (addresses are recomputed per stage from a few values: holding them all
-    // would cost registers the accumulators need)
-    const int xrow0 = m0 + 16 * wave + (lane >> 4);        // row of load i: xrow0 + 4i
-    // Weights: chunk e = 64*(8q + v) + lane for wave v's q-th weight load;
-    // e < 64*TT: code tile e/64, slot e%64; else scale tile (e-64TT)/8, part
-    // (e-64TT)%8.  LDS offset e*16 either way (codes then scales).
-    // loads this wave issues per stage (a weight load with no live lane is
-    // skipped): the wait for a stage leaves exactly the next stage's in flight
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
+    const __amdgpu_buffer_rsrc_t rc = make_rsrc(pcodes, (uint32_t)((int64_t)NT * KT * kTileCodeBytes));
+    const __amdgpu_buffer_rsrc_t rs = make_rsrc(pscales, (uint32_t)((int64_t)NT * KT * kTileScaleBytes));
+
+    // ---- stage loads: per-lane byte offsets of k-tile 0 ----------------------
+    // Activations: wave v, load i fills LDS bytes 1024*(4v+i) .. +1023, i.e.
+    // rows 16v + 4i + l/16; lane l fills position l%16 of its row, which holds
+    // chunk (l%16) ^ (row%16) (eight bf16, k = 8*chunk + 0..7).
+    uint32_t xoff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int row = m0 + 16 * wave + 4 * i + (lane >> 4);
+        const int chunk = (lane & 15) ^ ((4 * i + (lane >> 4)) & 15);
+        xoff[i] = row < M ? (uint32_t)(((int64_t)row * K + 8 * chunk) * 2) : kOutside;
+    }
+    // Weights: chunk e = 64*(8q + v) + lane for wave v's q-th load; e < 64*TT:
+    // code tile e/64, slot e%64; else scale tile (e-64TT)/8, part (e-64TT)%8.
+    // LDS offset e*16 either way (codes then scales).  A load is all codes or
+    // all scales (64*TT is a multiple of 64).
+    uint32_t woff[kWLoadsPerWave];
     int loads_per_stage = 4;
 #pragma unroll
-    for (int q = 0; q < kWLoadsPerWave; ++q)
+    for (int q = 0; q < kWLoadsPerWave; ++q) {
+        const int e = 64 * (8 * q + wave) + lane;
+        const bool code = 8 * q + wave < TT;
+        const int j = code ? e >> 6 : (e - 64 * TT) >> 3;
+        const int part = code ? (e & 63) : ((e - 64 * TT) & 7);
+        const int t = tile0 + j;
+        const int64_t tb = code ? kTileCodeBytes : kTileScaleBytes;
+        woff[q] = t < NT ? (uint32_t)((int64_t)t * KT * tb + part * 16) : kOutside;
         loads_per_stage += 64 * (8 * q + wave) < kWChunks ? 1 : 0;
-    const uint8_t *pc8 = reinterpret_cast<const uint8_t *>(pcodes);
-    const uint8_t *ps8 = reinterpret_cast<const uint8_t *>(pscales);
+    }
 
-    auto issue_stage = [&](int c, uint8_t *sx, uint8_t *sw) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            int grow = xrow0 + 4 * i;
-            grow = grow < M ? grow : M - 1;
-            const int chunk = (lane & 15) ^ ((4 * i + (lane >> 4)) & 15);
-            const int k = 128 * c + 8 * chunk;
-            const uint16_t *src = x + (int64_t)grow * K + (k < K ? k : 0);
-            __builtin_amdgcn_global_load_lds(src, sx + 1024 * (4 * wave + i), 16, 0, 0);
+    // One stage load n (0..3 activations, then weights) of k-tile c; adv is
+    // the byte advance of k-tile c (or kSkip, which puts every lane past the
+    // buffer end so the load only writes zeros into a free stage).
+    constexpr int kLoads = 4 + kWLoadsPerWave;
+    auto issue_load = [&](int n, int c, bool live, uint8_t *sx, uint8_t *sw) {
+        if (n < 4) {
+            const uint32_t adv = live ? 256u * c : kSkip;
+            load_lds16(rx, sx + 1024 * (4 * wave + n), xoff[n < 4 ? n : 0] + adv);
+        } else {
+            const int q = n - 4;
+            const bool code = 8 * q + wave < TT;
+            const uint32_t adv = live ? (code ? (uint32_t)kTileCodeBytes : (uint32_t)kTileScaleBytes) * c : kSkip;
+            if (64 * (8 * q + wave) + lane < kWChunks)
+                load_lds16(code ? rc : rs, sw + 1024 * (8 * q + wave), woff[q] + adv);
         }
+    };
+    auto issue_stage = [&](int c, bool live, uint8_t *sx, uint8_t *sw) {
 #pragma unroll
-        for (int q = 0; q < kWLoadsPerWave; ++q) {
-            const int e = 64 * (8 * q + wave) + lane;
-            if (e < kWChunks) {
-                const bool code = e < 64 * TT;
-                const int j = code ? e >> 6 : (e - 64 * TT) >> 3;
-                const int part = code ? (e & 63) : ((e - 64 * TT) & 7);
-                int t = tile0 + j;
-                t = t < NT ? t : NT - 1;                    // past NT: outputs never stored
-                const int64_t tc = (int64_t)t * KT + c;
-                const uint8_t *src = code ? pc8 + tc * kTileCodeBytes + part * 16
-                                          : ps8 + tc * kTileScaleBytes + part * 16;
-                __builtin_amdgcn_global_load_lds(src, sw + 1024 * (8 * q + wave), 16, 0, 0);
-            }
-        }
+        for (int n = 0; n < kLoads; ++n)
+            issue_load(n, c, live, sx, sw);
     };
 
     // ---- accumulators -------------------------------------------------------
+    // accF[j][i]: whole tile w*Q + j, row block (rb + i) & 7.
+    // accR[j][i]: remaining tile, row block rb + i.
     floatx4_t accF[Q > 0 ? Q : 1][8];
-    floatx4_t accR[RT > 0 ? RT : 1][2];
+    floatx4_t accR[RB > 0 ? RB : 1][RR];
 #pragma unroll
     for (int j = 0; j < Q; ++j)
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             accF[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int j = 0; j < RT; ++j)
+    for (int j = 0; j < RB; ++j)
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
+        for (int i = 0; i < RR; ++i)
             accR[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
     const bool ragged = (K & 127) != 0;
+    // code slots (r, 2h) and (r, 2h+1) hold this lane's k-values; the byte
+    // permute picks block 2d + gq/2 of each
+    const int h = gq & 1;
+    const uint32_t sel = (gq >> 1) ? 0x07060302u : 0x05040100u;
+    const int code_lane = (32 * h + r) * 16 + kh * 8;
+    const int scale_lane = r * 8 + kh * 4;
+    const int a_lane = r * 256;
 
     // ---- one k-tile from a landed stage -------------------------------------
     auto compute = [&](int c, uint8_t *sx, const uint8_t *sw, uint8_t *sxn, uint8_t *swn) {
         // wait for this stage (the next one may still be in flight), then
         // make every wave's loads of it visible; this wave's LDS reads of the
         // stage that is overwritten next are complete (lgkmcnt(0))
-        if (c + 1 < KT)
-            wait_vm(loads_per_stage);
-        else
-            wait_vm(0);
+        wait_vm(loads_per_stage);
         __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
-        if (c + 2 < KT)
-            issue_stage(c + 2, sxn, swn);                   // into the stage consumed at c-1
+        // the loads of k-tile c+2 (into the stage consumed at c-1) are spread
+        // over this k-tile's MFMAs: issued in one burst they stall the wave
+        // until the memory pipeline accepts them
+        const bool live = c + 2 < KT;
         if (ragged && c == KT - 1) {
             // zero the activation chunks past K of the last k-tile
             for (int s = (int)threadIdx.x; s < kBM * 16; s += 512) {
@@ -219,70 +229,66 @@ gemm_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
             __builtin_amdgcn_s_barrier();
         }
 
-        // this wave's code words and scales for its two k-steps: code words
-        // 2kh, 2kh+1 of the lane's slot, scales of blocks 4kh..4kh+3
-        uint2 cF[Q > 0 ? Q : 1], cR[RT > 0 ? RT : 1];
-        uint32_t sF[Q > 0 ? Q : 1], sR[RT > 0 ? RT : 1];
+        // code bytes of this wave's blocks 4kh..4kh+3 from the two slots, and
+        // their scales (shifted so block 4kh + 2dd + gq/2 sits in byte 2dd)
+        uint2 pF[Q > 0 ? Q : 1], qF[Q > 0 ? Q : 1], pR[RB > 0 ? RB : 1], qR[RB > 0 ? RB : 1];
+        uint32_t sF[Q > 0 ? Q : 1], sR[RB > 0 ? RB : 1];
 #pragma unroll
-        for (int j = 0; j < Q; ++j) {
-            const int jt = w * Q + j;
-            cF[j] = *reinterpret_cast<const uint2 *>(sw + jt * kTileCodeBytes + lane * 16 + kh * 8);
-            sF[j] = *reinterpret_cast<const uint32_t *>(sw + TT * kTileCodeBytes + jt * kTileScaleBytes + r * 8 + kh * 4);
+        for (int j = 0; j < Q + RB; ++j) {
+            const int jt = j < Q ? w * Q + j : (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + (j - Q));
+            const uint8_t *cb = sw + jt * kTileCodeBytes + code_lane;
+            const uint2 p = *reinterpret_cast<const uint2 *>(cb);
+            const uint2 q = *reinterpret_cast<const uint2 *>(cb + 256);
+            const uint32_t sv = *reinterpret_cast<const uint32_t *>(
+                                    sw + TT * kTileCodeBytes + jt * kTileScaleBytes + scale_lane) >> (8 * (gq >> 1));
+            if (j < Q) {
+                pF[j] = p; qF[j] = q; sF[j] = sv;
+            } else {
+                pR[j - Q] = p; qR[j - Q] = q; sR[j - Q] = sv;
+            }
         }
-#pragma unroll
-        for (int j = 0; j < RT; ++j) {
-            const int jt = 4 * Q + j;
-            cR[j] = *reinterpret_cast<const uint2 *>(sw + jt * kTileCodeBytes + lane * 16 + kh * 8);
-            sR[j] = *reinterpret_cast<const uint32_t *>(sw + TT * kTileCodeBytes + jt * kTileScaleBytes + r * 8 + kh * 4);
-        }
-
-        // A operand of row tile mt, k-step d: rows 16mt + r, the two 8-byte
-        // pieces k = 32d + 4gq + {0..3} and 32d + 16 + 4gq + {0..3}
-        auto read_a = [&](int d, int rowt) {
-            const int row = 16 * rowt + r;
-            const int c0 = 4 * d + (gq >> 1);
-            const uint8_t *base = sx + row * 256 + (gq & 1) * 8;
-            const uint2 lo = *reinterpret_cast<const uint2 *>(base + ((c0 ^ r) << 4));
-            const uint2 hi = *reinterpret_cast<const uint2 *>(base + (((c0 + 2) ^ r) << 4));
-            return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
-        };
 
 #pragma unroll
         for (int dd = 0; dd < 2; ++dd) {
             const int d = 2 * kh + dd;
             // B operands of every tile for this step, then one A operand at a
-            // time (fewer live registers than holding all eight A operands)
-            bf16x8_t bF[Q > 0 ? Q : 1], bR[RT > 0 ? RT : 1];
+            // time (fewer live registers than holding all eight)
+            bf16x8_t bF[Q > 0 ? Q : 1], bR[RB > 0 ? RB : 1];
 #pragma unroll
-            for (int j = 0; j < Q; ++j)
-                bF[j] = dd == 0 ? weight_operand_half<0>(cF[j], sF[j]) : weight_operand_half<1>(cF[j], sF[j]);
+            for (int j = 0; j < Q; ++j) {
+                const uint32_t wd = __builtin_amdgcn_perm(dd ? qF[j].y : qF[j].x, dd ? pF[j].y : pF[j].x, sel);
+                bF[j] = dequant8(wd, dd ? e4m3_to_f32<2>(sF[j]) : e4m3_to_f32<0>(sF[j]));
+            }
 #pragma unroll
-            for (int j = 0; j < RT; ++j)
-                bR[j] = dd == 0 ? weight_operand_half<0>(cR[j], sR[j]) : weight_operand_half<1>(cR[j], sR[j]);
+            for (int j = 0; j < RB; ++j) {
+                const uint32_t wd = __builtin_amdgcn_perm(dd ? qR[j].y : qR[j].x, dd ? pR[j].y : pR[j].x, sel);
+                bR[j] = dequant8(wd, dd ? e4m3_to_f32<2>(sR[j]) : e4m3_to_f32<0>(sR[j]));
+            }
+            const uint8_t *ab = sx + a_lane + (((4 * d + gq) ^ r) << 4);
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                const bf16x8_t a = read_a(d, mt);
+            for (int i = 0; i < 8; ++i) {
+                if ((8 * dd + i) % 2 == 0 && (8 * dd + i) / 2 < kLoads)
+                    issue_load((8 * dd + i) / 2, c + 2, live, sxn, swn);
+                const int mt = (rb + i) & 7;
+                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(ab + mt * 4096);
 #pragma unroll
                 for (int j = 0; j < Q; ++j)
-                    accF[j][mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bF[j], accF[j][mt], 0, 0, 0);
-            }
-            // this wave's rows of the remaining tiles (A operands re-read
-            // from LDS: indexing by the wave number would need scratch)
-            if (RT > 0) {
-                const bf16x8_t ar0 = read_a(d, 2 * w), ar1 = read_a(d, 2 * w + 1);
+                    accF[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bF[j], accF[j][i], 0, 0, 0);
+                if (i < RR) {
 #pragma unroll
-                for (int j = 0; j < RT; ++j) {
-                    accR[j][0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar0, bR[j], accR[j][0], 0, 0, 0);
-                    accR[j][1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ar1, bR[j], accR[j][1], 0, 0, 0);
+                    for (int j = 0; j < RB; ++j)
+                        accR[j][i < RR ? i : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            a, bR[j], accR[j][i < RR ? i : 0], 0, 0, 0);
                 }
             }
         }
     };
 
     // ---- pipeline: stages 0, 1 in flight, then one k-tile per step ----------
-    issue_stage(0, sx0, sw0);
-    if (KT > 1)
-        issue_stage(1, sx1, sw1);
+    // (every k-tile c issues the loads of c+2, skipped ones included, so the
+    // wait at k-tile c always leaves exactly one stage of loads in flight)
+    issue_stage(0, true, sx0, sw0);
+    issue_stage(1, KT > 1, sx1, sw1);
     for (int c = 0; c < KT; c += 3) {
         compute(c, sx0, sw0, sx2, sw2);
         if (c + 1 < KT)
@@ -294,10 +300,12 @@ gemm_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
     // ---- add the k-halves: waves 4..7 hand their sums to waves 0..3 --------
     {
         // every wave is past its last LDS read of the stages (the last
-        // compute ended with them), so the stage buffers are free
+        // compute ended with them) and its trailing zero-writing loads have
+        // landed, so the stage buffers are free
+        wait_vm(0);
         __builtin_amdgcn_s_waitcnt(0xc07f);
         __builtin_amdgcn_s_barrier();
-        constexpr int kAcc = 8 * Q + 2 * RT;                 // floatx4 per lane
+        constexpr int kAcc = 8 * Q + RB * RR;                // floatx4 per lane
         // one slot per wave pair: three activation stages and one weight
         // stage, each holding kPass fragments of 64 lanes x 16 bytes
         constexpr int kPass = kWStageBytes / (64 * 16);
@@ -308,7 +316,7 @@ gemm_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
             if (kh == 1) {
 #pragma unroll
                 for (int f = p0; f < kAcc && f < p0 + kPass; ++f)
-                    red[(f - p0) * 64 + lane] = f < 8 * Q ? accF[f >> 3][f & 7] : accR[(f - 8 * Q) >> 1][(f - 8 * Q) & 1];
+                    red[(f - p0) * 64 + lane] = f < 8 * Q ? accF[f >> 3][f & 7] : accR[(f - 8 * Q) / RR][(f - 8 * Q) % RR];
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_s_barrier();
@@ -318,7 +326,7 @@ gemm_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
                     if (f < 8 * Q)
                         accF[f >> 3][f & 7] += red[(f - p0) * 64 + lane];
                     else
-                        accR[(f - 8 * Q) >> 1][(f - 8 * Q) & 1] += red[(f - p0) * 64 + lane];
+                        accR[(f - 8 * Q) / RR][(f - 8 * Q) % RR] += red[(f - p0) * 64 + lane];
                 }
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
@@ -328,41 +336,43 @@ gemm_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
             return;
     }
 
-    // ---- epilogue: lane (r, gq) holds rows 4*gq + i of each 16-row M tile ----
+    // ---- epilogue: lane (r, gq) holds rows 4*gq + i of each 16-row block ----
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
         const int t = tile0 + w * Q + j;
         const int n = t * 16 + r;
         if (t < NT && n < N) {
 #pragma unroll
-            for (int mt = 0; mt < 8; ++mt)
+            for (int i = 0; i < 8; ++i) {
+                const int mt = (rb + i) & 7;
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = m0 + 16 * mt + 4 * gq + i;
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + 16 * mt + 4 * gq + e;
                     if (m < M)
-                        y[(int64_t)m * N + n] = g * accF[j][mt][i];
+                        y[(int64_t)m * ldy + n] = g * accF[j][i][e];
                 }
+            }
         }
     }
 #pragma unroll
-    for (int j = 0; j < RT; ++j) {
-        const int t = tile0 + 4 * Q + j;
+    for (int j = 0; j < RB; ++j) {
+        const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
         const int n = t * 16 + r;
         if (t < NT && n < N) {
 #pragma unroll
-            for (int i2 = 0; i2 < 2; ++i2)
+            for (int i = 0; i < RR; ++i)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int m = m0 + 16 * (2 * w + i2) + 4 * gq + i;
+                for (int e = 0; e < 4; ++e) {
+                    const int m = m0 + 16 * (rb + i) + 4 * gq + e;
                     if (m < M)
-                        y[(int64_t)m * N + n] = g * accR[j][i2][i];
+                        y[(int64_t)m * ldy + n] = g * accR[j][i][e];
                 }
         }
     }
 }
 
-typedef void (*gemm_fn)(const uint4 *, const uint2 *, float, const uint16_t *, float *, int, int,
-                        int, int, int, int);
+typedef void (*gemm_fn)(const uint8_t *, const uint8_t *, float, const uint16_t *, float *, int, int,
+                        int64_t, int, int, int);
 
 #define Q4P_GEMM_ENTRY(T) gemm_kernel<(T) / 4, (T) % 4>
 const gemm_fn kGemmTable[kMaxT + 1] = {
@@ -382,20 +392,41 @@ hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales
 {
     const int64_t NT = n_tiles(N);
     const int64_t KT = k_tiles(K);
-    const int64_t MB = (M + kBM - 1) / kBM;
-    // tiles per workgroup: about one workgroup per CU over the whole grid
-    int64_t T = (NT * MB + 255) / 256;
-    if (T < 1)
-        T = 1;
-    if (T > kMaxT)
-        T = kMaxT;
-    const int64_t NB = (NT + T - 1) / T;
-    const dim3 grid((unsigned)NB, (unsigned)MB), block(512);
-    hipLaunchKernelGGL(kGemmTable[T], grid, block, 0, stream,
-                       reinterpret_cast<const uint4 *>(packed_codes),
-                       reinterpret_cast<const uint2 *>(packed_scales), g, x, y, (int)M, (int)N,
-                       (int)K, (int)KT, (int)NT, (int)T);
-    return hipGetLastError();
+    // Buffer offsets are 32-bit: one launch covers at most 1 GiB of
+    // activations and of packed codes; larger problems run as several
+    // launches over row and tile ranges (y keeps its row stride N).
+    int64_t rows_per_launch = kMaxLaunchBytes / (K * 2);
+    rows_per_launch = rows_per_launch / kBM * kBM;
+    if (rows_per_launch > int64_t(65535) * kBM)
+        rows_per_launch = int64_t(65535) * kBM;
+    const int64_t tiles_per_launch = kMaxLaunchBytes / (KT * kTileCodeBytes);
+    if (rows_per_launch < 1 || tiles_per_launch < 1)
+        return hipErrorInvalidValue;                     // K beyond what one tile row allows
+    for (int64_t mb = 0; mb < M; mb += rows_per_launch) {
+        const int64_t Mc = M - mb < rows_per_launch ? M - mb : rows_per_launch;
+        const int64_t MB = (Mc + kBM - 1) / kBM;
+        for (int64_t tb = 0; tb < NT; tb += tiles_per_launch) {
+            const int64_t NTc = NT - tb < tiles_per_launch ? NT - tb : tiles_per_launch;
+            const int64_t Nc = N - 16 * tb < 16 * NTc ? N - 16 * tb : 16 * NTc;
+            // tiles per workgroup: about one workgroup per CU over the grid
+            int64_t T = (NTc * MB + 255) / 256;
+            if (T < 1)
+                T = 1;
+            if (T > kMaxT)
+                T = kMaxT;
+            const int64_t NB = (NTc + T - 1) / T;
+            const dim3 grid((unsigned)NB, (unsigned)MB), block(512);
+            hipLaunchKernelGGL(kGemmTable[T], grid, block, 0, stream,
+                               packed_codes + tb * KT * kTileCodeBytes,
+                               packed_scales + tb * KT * kTileScaleBytes, g, x + mb * K,
+                               y + mb * N + 16 * tb, (int)Mc, (int)Nc, N, (int)K, (int)KT,
+                               (int)NTc);
+            const hipError_t e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
 }
 
 }  // namespace q4p
