@@ -21,7 +21,10 @@
 //    the 128 activation rows and the workgroup's T packed code tiles and
 //    scale tiles are fetched with 16-byte buffer loads straight into one of
 //    three LDS stages, two k-tiles ahead of the MFMAs.  Offsets past the end
-//    of a buffer read as zero, which covers rows past M and tiles past N.
+//    of a buffer read as zero, which covers rows past M, tiles past N and
+//    activations past K (lanes whose chunk lies past K are pointed there), so
+//    the k-loop holds no LDS stores of its own: the compiler then tracks the
+//    stage loads per LDS array and waits only for the stage being read.
 //    Workgroup barriers are bare s_barrier with an explicit wait for the
 //    stage being consumed (a full barrier would also drain the loads of the
 //    stages in flight).
@@ -44,7 +47,11 @@ namespace {
 constexpr int kBM = 128;                       // activation rows per workgroup
 constexpr int kMaxT = 17;                      // weight tiles per workgroup
 constexpr int kXStageBytes = kBM * 256;        // one k-tile of activations
-constexpr int kWStageBytes = kMaxT * (kTileCodeBytes + kTileScaleBytes);
+// weight stage: the packed code and scale tiles of up to kMaxT tiles, rounded
+// up to whole 1 KB loads, plus 1 KB that loads with nothing to fetch write
+// their zeros into (so every wave issues the same loads, without branches)
+constexpr int kWDataBytes = (kMaxT * (kTileCodeBytes + kTileScaleBytes) + 1023) / 1024 * 1024;
+constexpr int kWStageBytes = kWDataBytes + 1024;
 // A buffer offset at or past a buffer's size reads as zero; this one marks
 // rows and tiles outside the problem (it stays past every buffer after the
 // per-stage advance, since one launch addresses less than 1 GiB per buffer).
@@ -134,19 +141,25 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     // Activations: wave v, load i fills LDS bytes 1024*(4v+i) .. +1023, i.e.
     // rows 16v + 4i + l/16; lane l fills position l%16 of its row, which holds
     // chunk (l%16) ^ (row%16) (eight bf16, k = 8*chunk + 0..7).
+    // Chunks past K (last k-tile of a ragged K) are pointed past the buffer
+    // end as well, so they land as zeros.
     uint32_t xoff[4];
+    int xk[4];                                             // k of the chunk within a k-tile
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = m0 + 16 * wave + 4 * i + (lane >> 4);
         const int chunk = (lane & 15) ^ ((4 * i + (lane >> 4)) & 15);
+        xk[i] = 8 * chunk;
         xoff[i] = row < M ? (uint32_t)(((int64_t)row * K + 8 * chunk) * 2) : kOutside;
     }
     // Weights: chunk e = 64*(8q + v) + lane for wave v's q-th load; e < 64*TT:
     // code tile e/64, slot e%64; else scale tile (e-64TT)/8, part (e-64TT)%8.
     // LDS offset e*16 either way (codes then scales).  A load is all codes or
-    // all scales (64*TT is a multiple of 64).
+    // all scales (64*TT is a multiple of 64).  Lanes past the last chunk read
+    // past the buffer end (zeros into the stage's rounding); a load with no
+    // chunk at all writes into the spare 1 KB.
     uint32_t woff[kWLoadsPerWave];
-    int loads_per_stage = 4;
+    int wlds[kWLoadsPerWave];
 #pragma unroll
     for (int q = 0; q < kWLoadsPerWave; ++q) {
         const int e = 64 * (8 * q + wave) + lane;
@@ -155,27 +168,27 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         const int part = code ? (e & 63) : ((e - 64 * TT) & 7);
         const int t = tile0 + j;
         const int64_t tb = code ? kTileCodeBytes : kTileScaleBytes;
-        woff[q] = t < NT ? (uint32_t)((int64_t)t * KT * tb + part * 16) : kOutside;
-        loads_per_stage += 64 * (8 * q + wave) < kWChunks ? 1 : 0;
+        woff[q] = t < NT && e < kWChunks ? (uint32_t)((int64_t)t * KT * tb + part * 16) : kOutside;
+        wlds[q] = 64 * (8 * q + wave) < kWChunks ? 1024 * (8 * q + wave) : kWDataBytes;
     }
 
     // One stage load n (0..3 activations, then weights) of k-tile c; adv is
     // the byte advance of k-tile c (or kSkip, which puts every lane past the
     // buffer end so the load only writes zeros into a free stage).
     constexpr int kLoads = 4 + kWLoadsPerWave;
-    auto issue_load = [&](int n, int c, bool live, uint8_t *sx, uint8_t *sw) {
+    auto issue_load = [&](int n, int c, bool live, uint8_t *sx, uint8_t *sw) __attribute__((always_inline)) {
         if (n < 4) {
+            const int i = n < 4 ? n : 0;
             const uint32_t adv = live ? 256u * c : kSkip;
-            load_lds16(rx, sx + 1024 * (4 * wave + n), xoff[n < 4 ? n : 0] + adv);
+            load_lds16(rx, sx + 1024 * (4 * wave + n), 128 * c + xk[i] < K ? xoff[i] + adv : kOutside);
         } else {
             const int q = n - 4;
             const bool code = 8 * q + wave < TT;
             const uint32_t adv = live ? (code ? (uint32_t)kTileCodeBytes : (uint32_t)kTileScaleBytes) * c : kSkip;
-            if (64 * (8 * q + wave) + lane < kWChunks)
-                load_lds16(code ? rc : rs, sw + 1024 * (8 * q + wave), woff[q] + adv);
+            load_lds16(code ? rc : rs, sw + wlds[q], woff[q] + adv);
         }
     };
-    auto issue_stage = [&](int c, bool live, uint8_t *sx, uint8_t *sw) {
+    auto issue_stage = [&](int c, bool live, uint8_t *sx, uint8_t *sw) __attribute__((always_inline)) {
 #pragma unroll
         for (int n = 0; n < kLoads; ++n)
             issue_load(n, c, live, sx, sw);
@@ -197,7 +210,6 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         for (int i = 0; i < RR; ++i)
             accR[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    const bool ragged = (K & 127) != 0;
     // code slots (r, 2h) and (r, 2h+1) hold this lane's k-values; the byte
     // permute picks block 2d + gq/2 of each
     const int h = gq & 1;
@@ -206,29 +218,21 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     const int scale_lane = r * 8 + kh * 4;
     const int a_lane = r * 256;
 
-    // ---- one k-tile from a landed stage -------------------------------------
-    auto compute = [&](int c, uint8_t *sx, const uint8_t *sw, uint8_t *sxn, uint8_t *swn) {
+    // ---- one k-tile per barrier (variants with four whole tiles per wave) ----
+    // Without double-buffered operands, for register room: after the barrier
+    // the wave reads its words, dequantises a k-step's operands and runs its
+    // MFMAs, twice.
+    auto compute = [&](int c, uint8_t *sx, const uint8_t *sw, uint8_t *sxn, uint8_t *swn) __attribute__((always_inline)) {
         // wait for this stage (the next one may still be in flight), then
         // make every wave's loads of it visible; this wave's LDS reads of the
         // stage that is overwritten next are complete (lgkmcnt(0))
-        wait_vm(loads_per_stage);
+        wait_vm(4 + kWLoadsPerWave);
         __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         // the loads of k-tile c+2 (into the stage consumed at c-1) are spread
         // over this k-tile's MFMAs: issued in one burst they stall the wave
         // until the memory pipeline accepts them
         const bool live = c + 2 < KT;
-        if (ragged && c == KT - 1) {
-            // zero the activation chunks past K of the last k-tile
-            for (int s = (int)threadIdx.x; s < kBM * 16; s += 512) {
-                const int row = s >> 4, chunk = (s & 15) ^ (row & 15);
-                if (128 * c + 8 * chunk >= K)
-                    *reinterpret_cast<uint4 *>(sx + 16 * s) = make_uint4(0u, 0u, 0u, 0u);
-            }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
-            __builtin_amdgcn_s_barrier();
-        }
-
         // code bytes of this wave's blocks 4kh..4kh+3 from the two slots, and
         // their scales (shifted so block 4kh + 2dd + gq/2 sits in byte 2dd)
         uint2 pF[Q > 0 ? Q : 1], qF[Q > 0 ? Q : 1], pR[RB > 0 ? RB : 1], qR[RB > 0 ? RB : 1];
@@ -284,9 +288,10 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         }
     };
 
-    // ---- pipeline: stages 0, 1 in flight, then one k-tile per step ----------
-    // (every k-tile c issues the loads of c+2, skipped ones included, so the
-    // wait at k-tile c always leaves exactly one stage of loads in flight)
+    auto run_single = [&]() __attribute__((always_inline)) {
+    // stages 0, 1 in flight, then one k-tile per step (every k-tile c issues
+    // the loads of c+2, skipped ones included, so the wait at k-tile c always
+    // leaves exactly one stage of loads in flight)
     issue_stage(0, true, sx0, sw0);
     issue_stage(1, KT > 1, sx1, sw1);
     for (int c = 0; c < KT; c += 3) {
@@ -296,6 +301,111 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         if (c + 2 < KT)
             compute(c + 2, sx2, sw2, sx1, sw1);
     }
+    };
+
+    // ---- software-pipelined k-loop --------------------------------------------
+    // NB operands per k-step: the Q whole tiles, then the wave's remaining
+    // tiles.  Raw code words and scales of one k-tile for this wave (pW, qW,
+    // sW) and the dequantised operands of its two k-steps (b0, b1).
+    constexpr int NB = Q + RB;
+    uint2 pW[NB], qW[NB];
+    uint32_t sW[NB];
+    bf16x8_t b0[NB], b1[NB];
+
+    // this wave's code bytes (blocks 4kh..4kh+3 of two slots) and scales of
+    // tile j of one landed stage; the scale of block 4kh + 2dd + gq/2 moved
+    // to byte 2dd
+    auto read_tile = [&](const uint8_t *sw, int j) __attribute__((always_inline)) {
+        const int jt = j < Q ? w * Q + j : (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + (j - Q));
+        const uint8_t *cb = sw + jt * kTileCodeBytes + code_lane;
+        pW[j] = *reinterpret_cast<const uint2 *>(cb);
+        qW[j] = *reinterpret_cast<const uint2 *>(cb + 256);
+        sW[j] = *reinterpret_cast<const uint32_t *>(
+                    sw + TT * kTileCodeBytes + jt * kTileScaleBytes + scale_lane) >> (8 * (gq >> 1));
+    };
+    // operand of tile j for the wave's k-step dd from the raw words
+    auto dequant_tile = [&](int j, int dd) __attribute__((always_inline)) {
+        const uint32_t wd = __builtin_amdgcn_perm(dd ? qW[j].y : qW[j].x, dd ? pW[j].y : pW[j].x, sel);
+        return dequant8(wd, dd ? e4m3_to_f32<2>(sW[j]) : e4m3_to_f32<0>(sW[j]));
+    };
+    // the MFMAs of the wave's k-step dd on the activations of stage sx with
+    // operands b; fill(i) is independent work placed after row block i
+    auto mfma_step = [&](int dd, const uint8_t *sx, const bf16x8_t *b, auto fill) __attribute__((always_inline)) {
+        const int d = 2 * kh + dd;
+        const uint8_t *ab = sx + a_lane + (((4 * d + gq) ^ r) << 4);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int mt = (rb + i) & 7;
+            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(ab + mt * 4096);
+#pragma unroll
+            for (int j = 0; j < Q; ++j)
+                accF[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], accF[j][i], 0, 0, 0);
+            if (i < RR) {
+#pragma unroll
+                for (int j = 0; j < RB; ++j)
+                    accR[j][i < RR ? i : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                        a, b[Q + j], accR[j][i < RR ? i : 0], 0, 0, 0);
+            }
+            fill(i);
+        }
+    };
+
+    // One k-tile c.  Phase 1: the MFMAs of the first k-step, with the second
+    // step's operands dequantised in between.  Then a barrier: stage c+1 has
+    // landed everywhere and every wave is done with stage c-1.  Phase 2: the
+    // MFMAs of the second k-step, with the stage loads of k-tile c+2 (into the
+    // stage of c-1) and the reading and dequantising of k-tile c+1's first
+    // step in between.  So no wave ever waits for its own dequantisation, and
+    // each stage has about one k-tile to land.
+    auto ktile = [&](int c, const uint8_t *sxc, const uint8_t *swn, uint8_t *sxl, uint8_t *swl) __attribute__((always_inline)) {
+        mfma_step(0, sxc, b0, [&](int i) __attribute__((always_inline)) {
+            if (i < NB)
+                b1[i < NB ? i : 0] = dequant_tile(i < NB ? i : 0, 1);
+        });
+        wait_vm(0);
+        __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0)
+        __builtin_amdgcn_s_barrier();
+        const bool live = c + 2 < KT;
+        mfma_step(1, sxc, b1, [&](int i) __attribute__((always_inline)) {
+            if (i < kLoads)
+                issue_load(i, c + 2, live, sxl, swl);
+            // tile i's words are read two row blocks before they are used
+            if (i < NB)
+                read_tile(swn, i < NB ? i : 0);
+            if (i >= 2 && i - 2 < NB)
+                b0[i >= 2 && i - 2 < NB ? i - 2 : 0] = dequant_tile(i >= 2 && i - 2 < NB ? i - 2 : 0, 0);
+        });
+        static_assert(NB <= 6, "every tile is dequantised inside the row loop");
+    };
+
+    auto run_pipelined = [&]() __attribute__((always_inline)) {
+    // stages 0 and 1 (skipped past the last k-tile) land before the loop;
+    // afterwards every k-tile issues the loads of the k-tile two ahead
+    issue_stage(0, true, sx0, sw0);
+    issue_stage(1, KT > 1, sx1, sw1);
+    wait_vm(0);
+    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_barrier();
+#pragma unroll
+    for (int j = 0; j < NB; ++j) {
+        read_tile(sw0, j);
+        b0[j] = dequant_tile(j, 0);
+    }
+    for (int c = 0; c < KT; c += 3) {
+        ktile(c, sx0, sw1, sx2, sw2);
+        if (c + 1 < KT)
+            ktile(c + 1, sx1, sw2, sx0, sw0);
+        if (c + 2 < KT)
+            ktile(c + 2, sx2, sw0, sx1, sw1);
+    }
+    };
+
+    // Double-buffered operands need about 40 more registers than fit beside
+    // the accumulators of four whole tiles.
+    if constexpr (Q >= 4)
+        run_single();
+    else
+        run_pipelined();
 
     // ---- add the k-halves: waves 4..7 hand their sums to waves 0..3 --------
     {
@@ -311,6 +421,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         constexpr int kPass = kWStageBytes / (64 * 16);
         floatx4_t *red = reinterpret_cast<floatx4_t *>(w < 2 ? (w == 0 ? sx0 : sx1) : (w == 2 ? sx2 : sw0));
         static_assert(kWStageBytes <= kXStageBytes, "pass size bounded by the smaller stage");
+        static_assert(3 * (kXStageBytes + kWStageBytes) <= 160 * 1024, "LDS of one CU");
 #pragma unroll
         for (int p0 = 0; p0 < kAcc; p0 += kPass) {
             if (kh == 1) {
