@@ -71,10 +71,15 @@ size_t q4proj_packed_codes_bytes(int64_t N, int64_t K);
 size_t q4proj_packed_scales_bytes(int64_t N, int64_t K);
 
 /*
- * Device scratch q4proj_gemv needs for (M, N, K): 512 KiB for 1 <= M <= 16
- * (valid N, K), 0 otherwise; q4proj_gemm needs none and ignores its workspace.
+ * Device scratch q4proj_gemv needs for (M, N, K), 1 <= M <= 16 (valid N, K):
+ *     8 * (65536 + (KS - 1) * M * N) bytes,
+ * where KS (1, 2, 4 or 8) is the number of ranges K is cut into so that one
+ * range's activations fit in on-chip memory: KS = 1 while M * ceil(K/128) *
+ * 256 <= 128 KiB (e.g. every M = 1 shape up to K = 65536), KS = 2 for M = 7 at
+ * K = 17408.  0 otherwise; q4proj_gemm needs none and ignores its workspace.
  * The gemv workspace holds one 64-bit exchange word per output of the row
- * tiles that two workgroups share.  Ownership and state:
+ * tiles that two workgroups share, and per output and join of the K ranges'
+ * partial results.  Ownership and state:
  *   - owned by the caller, 8-byte aligned, not overlapping any other argument;
  *   - zero-filled by the caller before its first use; every call that
  *     completes leaves it zero-filled again, so it is reused as is;

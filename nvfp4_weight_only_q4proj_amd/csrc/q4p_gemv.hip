@@ -381,6 +381,14 @@ gemv_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
 // the flag set adds the two partials -- fp32 addition of two values is
 // commutative, so the result does not depend on which side comes second --
 // stores y and clears the word for the next call.  No fences, no waiting.
+//
+// When the activations of all of K do not fit, K is cut into KS ranges (a
+// power of two) that do, each streamed as above by its own G/KS workgroups.
+// The KS partial results of an output are then joined along a fixed binary
+// tree of the same two-party exchanges (ranges 2i and 2i+1 first, then pairs
+// of pairs, ...): each join adds two values, so the total does not depend on
+// arrival order either.  The tree's words follow the boundary words in the
+// workspace, one per output and join.
 
 constexpr int kSkMaxGroups = 256;
 constexpr int kSkMaxWaves = 8;
@@ -389,10 +397,12 @@ constexpr int kSkXMaxBytes = 128 * 1024;       // + 16 KB of partial sums stays 
 constexpr int kSkLdsFloor = 96 * 1024;
 constexpr int kSkStage = 8;                    // 16-byte activation loads per lane before the ring
 
+constexpr int kSkMaxRanges = 8;               // K ranges joined by the exchange tree
+constexpr int64_t kSkBoundaryWords = (int64_t)kSkMaxGroups * 64 * 4;
+
 struct SkArgs {
-    int U;                                     // units = NT * KT (< 2^31)
-    int base, rem;                             // U / G, U % G
     int M, N, K, KT, NT, G, WPG;
+    int KS, KTR;                               // K ranges, k-tiles per range (last may be shorter)
     float g;
 };
 
@@ -407,16 +417,25 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int gq = lane >> 4;
-    const int G = a.G, WPG = a.WPG, KT = a.KT, M = a.M, K = a.K;
+    const int G = a.G, WPG = a.WPG, KTG = a.KT, M = a.M, K = a.K;
 
     // workgroups are dealt round-robin to the 8 XCDs: give consecutive ranges
     // to workgroups on the same XCD
     const int b = blockIdx.x;
-    const int L = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
-    // balanced split: the first `rem` groups (and, inside a group, the first
+    const int LG = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+    // K range of this workgroup: k-tiles c0 .. c0 + KT - 1, streamed by the
+    // GR workgroups of that range; below, units, KT and L are range-local
+    const int GR = G / a.KS;
+    const int kr = LG / GR;
+    const int L = LG - kr * GR;
+    const int c0 = kr * a.KTR;
+    const int KT = KTG - c0 < a.KTR ? KTG - c0 : a.KTR;
+    const int U = a.NT * KT;
+    const int ubase = U / GR, urem = U - ubase * GR;
+    // balanced split: the first `urem` groups (and, inside a group, the first
     // `wr` waves) take one unit more
-    const int UW0 = L * a.base + (L < a.rem ? L : a.rem);
-    const int UWn = a.base + (L < a.rem ? 1 : 0);
+    const int UW0 = L * ubase + (L < urem ? L : urem);
+    const int UWn = ubase + (L < urem ? 1 : 0);
     const int UW1 = UW0 + UWn;
     const int wb = UWn / WPG, wr = UWn - wb * WPG;
     auto wave_start = [&](int v) { return UW0 + v * wb + (v < wr ? v : wr); };
@@ -434,9 +453,10 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     uint8_t *zstrip = smem + xbytes;
     floatx4_t *part = reinterpret_cast<floatx4_t *>(smem + xbytes + kZeroBytes);
 
-    // 1. activation staging loads (all of x: rows < M, every k-tile)
+    // 1. activation staging loads (rows < M, the k-tiles of this range)
     const int nthr = 64 * WPG;
     const int gpr = KT * 16;                   // 16-byte groups per activation row
+    const int kbase = c0 * 128;
     const int ngroups = M * gpr;
     // group tid + i*nthr is (row srow[i], group sq[i] of that row): walk the
     // rows instead of dividing
@@ -458,7 +478,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
 #pragma unroll
     for (int i = 0; i < kSkStage; ++i) {
         xs[i] = make_uint4(0u, 0u, 0u, 0u);
-        const int k = sq[i] * 8;
+        const int k = kbase + sq[i] * 8;
         if (srow[i] < M && k < K)
             xs[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)srow[i] * K + k);
     }
@@ -468,14 +488,24 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const uint2 *ps = pscales + r;
     uint4 cw[PF];
     uint2 sw[PF];
-    auto load = [&](int s, int u) {
-        const int j = u <= ulast ? u : ulast;
-        cw[s] = load_stream16(pc + (int64_t)j * 64);
-        sw[s] = ps[(int64_t)j * 16];
+    // next unit to load, as (row tile, range-local k-tile); loads past the
+    // wave's last unit re-read it, so the ring stays unconditional
+    int ld_u = u0, ld_t = n > 0 ? u0 / KT : 0, ld_c = n > 0 ? u0 - ld_t * KT : 0;
+    auto load = [&](int s) {
+        const int64_t j = (int64_t)ld_t * KTG + c0 + ld_c;
+        cw[s] = load_stream16(pc + j * 64);
+        sw[s] = ps[j * 16];
+        if (ld_u < ulast) {
+            ++ld_u;
+            if (++ld_c == KT) {
+                ld_c = 0;
+                ++ld_t;
+            }
+        }
     };
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
-        load(s, u0 + s);
+        load(s);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -500,7 +530,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             }
             if (row >= M)
                 break;
-            const int k = q * 8;
+            const int k = kbase + q * 8;
             put(row, q, k < K ? *reinterpret_cast<const uint4 *>(x + (int64_t)row * K + k)
                               : make_uint4(0u, 0u, 0u, 0u));
             q += nthr;
@@ -519,14 +549,36 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int cfirst = n > 0 ? u0 - tfirst * KT : 0;
     int t = tfirst, c = cfirst;
 
+    // This range's complete value v of output (m, col) (col < N): joined with
+    // the other ranges' values along the tree -- at each level the side that
+    // finds its partner's value adds the two, clears the word and goes on --
+    // and stored by the last join (at once when there is one range).
+    auto join = [&](int m, int col, float v) {
+        for (int span = 1; span < a.KS; span *= 2) {
+            const int set = (a.KS - a.KS / span) + kr / (2 * span);
+            unsigned long long *wd = xch + kSkBoundaryWords + ((int64_t)set * M + m) * N + col;
+            const unsigned long long mine =
+                (1ull << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, v);
+            const unsigned long long old =
+                __hip_atomic_exchange(wd, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (!(old >> 32))
+                return;                                 // the partner side goes on
+            v = __builtin_bit_cast(float, (uint32_t)old) + v;
+            __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        y[(int64_t)m * N + col] = g * v;
+    };
     auto store_y = [&](int tt, const floatx4_t &v) {
         const int col = 16 * tt + r;
         if (col < N) {
 #pragma unroll
             for (int j = 0; j < ROWS; ++j) {
                 const int m = 4 * gq + j;
+                // copy the element out first: clang mis-lowers a bit_cast whose
+                // operand is a vector element (it reads element 0)
+                const float vj = v[j];
                 if (m < M)
-                    y[(int64_t)m * N + col] = g * v[j];
+                    join(m, col, vj);
             }
         }
     };
@@ -572,7 +624,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                     }
                 }
             }
-            load(s, u0 + i + s + PF);
+            load(s);
             __builtin_amdgcn_sched_barrier(0);
         }
     }
@@ -605,7 +657,8 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             store_y(tau, sum);
             continue;
         }
-        const int bnd = ta < UW0 ? L - 1 : L;           // boundary between groups bnd, bnd + 1
+        // boundary between groups bnd, bnd + 1 of this range
+        const int bnd = kr * GR + (ta < UW0 ? L - 1 : L);
         unsigned long long *slot = xch + ((int64_t)bnd * 64 + lane) * 4;
         const int col = 16 * tau + r;
 #pragma unroll
@@ -621,9 +674,9 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                     slot + j, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                 if (old >> 32) {
                     const float other = __builtin_bit_cast(float, (uint32_t)old);
-                    if (col < N)
-                        y[(int64_t)m * N + col] = g * (other + sj);
                     __hip_atomic_store(slot + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (col < N)
+                        join(m, col, other + sj);
                 }
             }
         }
@@ -751,6 +804,26 @@ gemv_sk_fn pick_sk_kernel(int64_t M)
     }
 }
 
+// K ranges for the stream-K kernel: the fewest (a power of two) whose
+// activations fit in LDS.
+int64_t sk_ranges(int64_t M, int64_t K)
+{
+    const int64_t KT = k_tiles(K);
+    int64_t KS = 1;
+    while (KS < kSkMaxRanges && M * ((KT + KS - 1) / KS) * 256 > kSkXMaxBytes)
+        KS *= 2;
+    return KS;
+}
+
+// The stream-K kernel serves a shape when its ranges' activations fit in LDS,
+// every range gets at least one k-tile, and unit indices stay below 2^31.
+bool sk_usable(int64_t M, int64_t N, int64_t K)
+{
+    const int64_t KT = k_tiles(K), NT = n_tiles(N), KS = sk_ranges(M, K);
+    const int64_t KTR = (KT + KS - 1) / KS;
+    return M * KTR * 256 <= kSkXMaxBytes && KT - (KS - 1) * KTR >= 1 && NT * KT < ((int64_t)1 << 31);
+}
+
 struct SkPlan {
     gemv_sk_fn fn;
     SkArgs args;
@@ -762,20 +835,25 @@ struct SkPlan {
 // row tile is shared by at most two workgroups.
 SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t KT = k_tiles(K), NT = n_tiles(N), U = NT * KT;   // U < 2^31 (checked by the caller)
-    int64_t G = device_cus();
-    if (G > kSkMaxGroups)
-        G = kSkMaxGroups;
-    if (G > NT)
-        G = NT;
+    const int64_t KT = k_tiles(K), NT = n_tiles(N);
+    const int64_t KS = sk_ranges(M, K);
+    const int64_t KTR = (KT + KS - 1) / KS;
+    int64_t GR = device_cus() / KS;                     // workgroups per K range
+    if (GR > kSkMaxGroups / KS)
+        GR = kSkMaxGroups / KS;
+    if (GR > NT)
+        GR = NT;
+    if (GR < 1)
+        GR = 1;
+    const int64_t ULAST = NT * (KT - (KS - 1) * KTR);   // units of the shortest range
     int64_t WPG = kSkMaxWaves;
-    if (WPG > U / G)
-        WPG = U / G;
+    if (WPG > ULAST / GR)
+        WPG = ULAST / GR;
     SkPlan p;
     p.fn = pick_sk_kernel(M);
-    p.args = SkArgs{(int)U, (int)(U / G), (int)(U % G), (int)M, (int)N, (int)K, (int)KT, (int)NT,
-                    (int)G, (int)WPG, 0.f};
-    size_t lds = (size_t)(M * KT * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
+    p.args = SkArgs{(int)M, (int)N, (int)K, (int)KT, (int)NT, (int)(GR * KS), (int)WPG, (int)KS,
+                    (int)KTR, 0.f};
+    size_t lds = (size_t)(M * KTR * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
     if (lds < (size_t)kSkLdsFloor)
         lds = kSkLdsFloor;
     p.lds = lds;
@@ -809,11 +887,10 @@ SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K)
 
 size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
-    (void)N;
-    (void)K;
-    if (M < 1 || M > 16)
+    if (M < 1 || M > 16 || N < 1 || K < 1)
         return 0;
-    return (size_t)kSkMaxGroups * 64 * 4 * sizeof(unsigned long long);
+    const int64_t KS = sk_usable(M, N, K) ? sk_ranges(M, K) : 1;
+    return (size_t)(kSkBoundaryWords + (KS - 1) * M * N) * sizeof(unsigned long long);
 }
 
 hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
@@ -821,7 +898,7 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        void *workspace, hipStream_t stream)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
-    if (M * KT * 256 <= kSkXMaxBytes && NT * KT < ((int64_t)1 << 31)) {
+    if (sk_usable(M, N, K)) {
         const SkPlan p = cached_sk_plan(M, N, K);
         SkArgs args = p.args;
         args.g = g;

@@ -46,10 +46,23 @@ def test_packed_sizes(q4, N, K):
     nt, kt = -(-N // 16), -(-K // 128)
     assert q4.q4proj_packed_codes_bytes(N, K) == nt * kt * 1024 >= N * K // 2
     assert q4.q4proj_packed_scales_bytes(N, K) == nt * kt * 128 >= N * K // 16
-    # gemv's exchange words: one 64-bit word x 4 rows x 64 lanes per workgroup boundary
-    assert q4.q4proj_workspace_bytes(1, N, K) == q4.q4proj_workspace_bytes(16, N, K) == 512 * 1024
+    # gemv's exchange words: one 64-bit word x 4 rows x 64 lanes per workgroup
+    # boundary (256 at most), plus, when K is cut into KS ranges so that a
+    # range's activations (M x k-tiles x 256 B) fit in 128 KiB, one word per
+    # output for each of the KS - 1 joins
+    for M in (1, 7, 16):
+        ks = 1
+        while ks < 8 and M * -(-kt // ks) * 256 > 128 * 1024:
+            ks *= 2
+        assert q4.q4proj_workspace_bytes(M, N, K) == 512 * 1024 + 8 * (ks - 1) * M * N
     assert q4.q4proj_workspace_bytes(17, N, K) == 0
     assert q4.q4proj_workspace_bytes(512, N, K) == 0
+
+
+def test_workspace_of_the_verify_shape(q4):
+    # M = 7 at K = 17408: 244 KB of activations -> two K ranges, one join
+    assert q4.q4proj_workspace_bytes(7, 5120, 17408) == 512 * 1024 + 8 * 7 * 5120
+    assert q4.q4proj_workspace_bytes(7, 17408, 5120) == 512 * 1024
 
 
 @pytest.mark.parametrize("N,K", [(0, 16), (16, 0), (16, 8), (16, 24), (-1, 16)])
