@@ -406,7 +406,7 @@ struct SkArgs {
     float g;
 };
 
-template <int ROWS, int PF>
+template <int ROWS, int PF, bool KR>
 __global__ void __launch_bounds__(64 * kSkMaxWaves)
 gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
                const uint16_t *__restrict__ x, float *__restrict__ y,
@@ -488,19 +488,25 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const uint2 *ps = pscales + r;
     uint4 cw[PF];
     uint2 sw[PF];
-    // next unit to load, as (row tile, range-local k-tile); loads past the
-    // wave's last unit re-read it, so the ring stays unconditional
-    int ld_u = u0, ld_t = n > 0 ? u0 / KT : 0, ld_c = n > 0 ? u0 - ld_t * KT : 0;
+    // next unit to load; loads past the wave's last unit re-read it, so the
+    // ring stays unconditional.  With K ranges (KR) a unit's packed index is
+    // t*KTG + c0 + c for (row tile t, range-local k-tile c), walked
+    // incrementally; with one range it is the unit itself.
+    int ld_u = u0, ld_t = KR && n > 0 ? u0 / KT : 0, ld_c = KR && n > 0 ? u0 - ld_t * KT : 0;
     auto load = [&](int s) {
-        const int64_t j = (int64_t)ld_t * KTG + c0 + ld_c;
+        const int64_t j = KR ? (int64_t)ld_t * KTG + c0 + ld_c : (int64_t)ld_u;
         cw[s] = load_stream16(pc + j * 64);
         sw[s] = ps[j * 16];
-        if (ld_u < ulast) {
-            ++ld_u;
-            if (++ld_c == KT) {
-                ld_c = 0;
-                ++ld_t;
+        if (KR) {
+            if (ld_u < ulast) {
+                ++ld_u;
+                if (++ld_c == KT) {
+                    ld_c = 0;
+                    ++ld_t;
+                }
             }
+        } else {
+            ld_u = ld_u < ulast ? ld_u + 1 : ulast;
         }
     };
 #pragma unroll
@@ -794,14 +800,20 @@ Plan cached_plan(int64_t M, int64_t N, int64_t K)
 typedef void (*gemv_sk_fn)(const uint4 *, const uint2 *, const uint16_t *, float *,
                            unsigned long long *, SkArgs);
 
-gemv_sk_fn pick_sk_kernel(int64_t M)
+template <bool KR>
+gemv_sk_fn pick_sk_kernel_k(int64_t M)
 {
     switch (M) {
-    case 1: return gemv_sk_kernel<1, kSkPrefetch>;
-    case 2: return gemv_sk_kernel<2, kSkPrefetch>;
-    case 3: return gemv_sk_kernel<3, kSkPrefetch>;
-    default: return gemv_sk_kernel<4, kSkPrefetch>;
+    case 1: return gemv_sk_kernel<1, kSkPrefetch, KR>;
+    case 2: return gemv_sk_kernel<2, kSkPrefetch, KR>;
+    case 3: return gemv_sk_kernel<3, kSkPrefetch, KR>;
+    default: return gemv_sk_kernel<4, kSkPrefetch, KR>;
     }
+}
+
+gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges)
+{
+    return ranges ? pick_sk_kernel_k<true>(M) : pick_sk_kernel_k<false>(M);
 }
 
 // K ranges for the stream-K kernel: the fewest (a power of two) whose
@@ -850,7 +862,7 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K)
     if (WPG > ULAST / GR)
         WPG = ULAST / GR;
     SkPlan p;
-    p.fn = pick_sk_kernel(M);
+    p.fn = pick_sk_kernel(M, KS > 1);
     p.args = SkArgs{(int)M, (int)N, (int)K, (int)KT, (int)NT, (int)(GR * KS), (int)WPG, (int)KS,
                     (int)KTR, 0.f};
     size_t lds = (size_t)(M * KTR * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
