@@ -16,7 +16,9 @@ Also measured and reported in the same JSON line:
                 `traffic` from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary in
                 profiles/ when it was taken on the current kernel source.
   prefill_gemm  the M = 512 prefill chunk (qkv 5120->14336, gate/up
-                5120->17408): TFLOP/s vs 2.517 PFLOP/s dense bf16.
+                5120->17408): TFLOP/s vs 2.517 PFLOP/s dense bf16; its
+                `traffic` (HBM bytes per launch, mean of the two) from the
+                rocprofv3 counter summary in profiles/ when current.
   shapes        the other workloads' GEMVs (M = 7 verify, lm-head, 4B shapes).
   pack          the one-time weight swizzle (read + write bytes / s).
   cpu_baseline  the CPU oracle on the decode step, on the host cores.
@@ -225,7 +227,9 @@ def main():
             "roofline": {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(tflops, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
-                         "traffic": None, "kernel_source_sha256_16": src_digest("q4p_gemm.hip")},
+                         "traffic": read_traffic("gemm_pre_counters.txt", src_digest("q4p_gemm.hip"),
+                                                 None),
+                         "kernel_source_sha256_16": src_digest("q4p_gemm.hip")},
             "tokens_per_s": round(512 / (tot_ms * 1e-3), 1),
             "per_matrix": per, "steps": gsteps}
         del pre_u
