@@ -7,33 +7,43 @@
 //    and T weight-row tiles of 16 (BN = 16*T).  T is chosen so the grid has
 //    about one workgroup per CU (256), e.g. T = 17 for N = 17408 and T = 14
 //    for N = 14336 at M = 512: 256 equal workgroups, no tail wave.
-//  * Waves w and w+4 own the same outputs and split every k-tile: wave w
-//    takes its first two 32-wide k-steps, wave w+4 the last two, and the two
-//    partial sums are added through LDS at the end.  Two waves per SIMD let
-//    one wave's dequantisation and LDS waits overlap the other's MFMAs.
+//  * Waves w and w+4 (one SIMD) own the same outputs and split every k-tile:
+//    wave w takes its first two 32-wide k-steps, wave w+4 the last two, and
+//    the two partial sums are added through LDS at the end.
 //  * Each wave pair owns Q = T/4 whole weight tiles (all 128 rows) plus a
 //    share of the RT = T%4 remaining tiles: half of one tile (64 rows) when
 //    RT = 2, a quarter (32 rows) of each otherwise, so all waves do the same
 //    number of MFMAs whatever T is.  A wave walks the eight 16-row blocks of
-//    activations starting at its share of the remaining tiles, so those
-//    MFMAs reuse the activation operands it reads anyway.
+//    activations starting with its rows of the remaining tiles (block i ^ rb
+//    for i = 0..7), so those MFMAs reuse the activation operands it reads
+//    anyway.
 //  * Operands reach LDS without passing through registers: per k-tile (128 k)
 //    the 128 activation rows and the workgroup's T packed code tiles and
 //    scale tiles are fetched with 16-byte buffer loads straight into one of
-//    three LDS stages, two k-tiles ahead of the MFMAs.  Offsets past the end
-//    of a buffer read as zero, which covers rows past M, tiles past N and
-//    activations past K (lanes whose chunk lies past K are pointed there), so
-//    the k-loop holds no LDS stores of its own: the compiler then tracks the
-//    stage loads per LDS array and waits only for the stage being read.
-//    Workgroup barriers are bare s_barrier with an explicit wait for the
-//    stage being consumed (a full barrier would also drain the loads of the
-//    stages in flight).
+//    three LDS stages.  Offsets past the end of a buffer read as zero, which
+//    covers rows past M, tiles past N and activations past K (lanes whose
+//    chunk lies past K are pointed there), so the k-loop holds no LDS stores
+//    of its own: the compiler then tracks the stage loads per LDS array and
+//    never drains loads of a stage it is not reading.  Every wave issues the
+//    same branch-free loads (a load with nothing to fetch writes zeros into a
+//    spare 1 KB), with the k-tile advance in the scalar offset.
 //  * MFMA k-order: in 16x16x32 step d, lane (r, gq) supplies k = 32d + 8gq
 //    + 0..7, i.e. one 16-byte chunk of an activation row (one ds_read_b128).
 //    Chunks are XOR-swizzled by row within LDS so the rows one read touches
 //    fall in different banks.  The matching eight weight codes are halves of
 //    two code slots of the packed tile (one byte permute); they share one
 //    e4m3 scale.
+//  * Software pipeline: a wave's operands for its second k-step are
+//    dequantised between the MFMAs of its first; one workgroup barrier per
+//    k-tile sits between the two steps (past it, stage c+1 has landed
+//    everywhere and stage c-1 is free); during the second step the loads of
+//    k-tile c+2 go out and the next k-tile's code words are read and its
+//    first step dequantised.  The matrix core never waits for a wave's own
+//    dequantisation, only for issue slots: on gfx950 VALU work beside the
+//    MFMAs of the same SIMD costs about half its cycles on top of theirs, so
+//    the VALU count per MFMA is what the loop is written to keep low
+//    (per-step base addresses plus immediate offsets, no per-load address
+//    arithmetic).
 //  * Dequantisation to bf16 with the e4m3 scale folded in is exact: q*s has
 //    at most 6 significant bits.  fp32 accumulation in the MFMA; y = g * acc
 //    stored once.
@@ -57,9 +67,6 @@ constexpr int kWStageBytes = kWDataBytes + 1024;
 // per-stage advance, since one launch addresses less than 1 GiB per buffer).
 constexpr uint32_t kOutside = 0x80000000u;
 constexpr int64_t kMaxLaunchBytes = int64_t(1) << 30;
-// Stage-load advance that lands every lane past the end of its buffer (a
-// load past the last k-tile then only writes zeros to a free stage).
-constexpr uint32_t kSkip = 0x40000000u;
 
 // Raw buffer resource over `bytes` bytes at p (gfx9 dword 3 for untyped
 // 32-bit-element access; offsets are checked against `bytes`).
@@ -68,10 +75,14 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), 0, (int)bytes, 0x00020000);
 }
 
-__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds, uint32_t voffset)
+// 16 bytes per lane from rsrc at voffset + soffset into LDS at lds + 16*lane.
+// Lanes are marked outside the buffer through voffset alone; soffset carries
+// the k-tile advance and never leads a lane past the buffer on its own.
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rsrc, uint8_t *lds, uint32_t voffset,
+                                           uint32_t soffset)
 {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset, 0, 0, 0);
+        rsrc, (__attribute__((address_space(3))) void *)lds, 16, voffset, soffset, 0, 0);
 }
 
 // Eight e2m1 codes (one dword, low nibble first) times one decoded scale.
@@ -85,20 +96,10 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t wd, float s)
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
-// gfx9 s_waitcnt immediate: wait until at most n vector-memory operations of
-// this wave are outstanding (expcnt and lgkmcnt left alone)
-__device__ __forceinline__ void wait_vm(int n)
-{
-    switch (n) {
-#define Q4P_VM(k) \
-    case k: __builtin_amdgcn_s_waitcnt(0x0f70 | ((k) & 15) | (((k) >> 4) << 14)); break;
-        Q4P_VM(0) Q4P_VM(1) Q4P_VM(2) Q4P_VM(3) Q4P_VM(4) Q4P_VM(5) Q4P_VM(6) Q4P_VM(7)
-        Q4P_VM(8) Q4P_VM(9) Q4P_VM(10) Q4P_VM(11) Q4P_VM(12) Q4P_VM(13) Q4P_VM(14) Q4P_VM(15)
-        Q4P_VM(16) Q4P_VM(17) Q4P_VM(18) Q4P_VM(19) Q4P_VM(20)
-#undef Q4P_VM
-    default: __builtin_amdgcn_s_waitcnt(0x0f70); break;
-    }
-}
+// gfx9 s_waitcnt immediates: vmcnt(0) (expcnt and lgkmcnt left alone) and
+// lgkmcnt(0)
+constexpr int kWaitVm0 = 0x0f70;
+constexpr int kWaitLgkm0 = 0xc07f;
 
 template <int Q, int RT>
 __global__ void __launch_bounds__(512)
@@ -131,26 +132,28 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     const int tile0 = blockIdx.x * TT;
     // first 16-row block of this wave's share of the remaining tiles; the
     // wave visits row blocks rb, rb+1, ... (mod 8)
-    const int rb = RT == 2 ? 4 * (w & 1) : 2 * w;
+    const int rb = RT == 0 ? 0 : RT == 2 ? 4 * (w & 1) : 2 * w;
 
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(x, (uint32_t)((int64_t)M * K * 2));
-    const __amdgpu_buffer_rsrc_t rc = make_rsrc(pcodes, (uint32_t)((int64_t)NT * KT * kTileCodeBytes));
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(pscales, (uint32_t)((int64_t)NT * KT * kTileScaleBytes));
+    // buffer sizes (a load past the last k-tile gets size 0: all zeros)
+    const uint32_t xbytes = (uint32_t)((int64_t)M * K * 2);
+    const uint32_t cbytes = (uint32_t)((int64_t)NT * KT * kTileCodeBytes);
+    const uint32_t sbytes = (uint32_t)((int64_t)NT * KT * kTileScaleBytes);
 
     // ---- stage loads: per-lane byte offsets of k-tile 0 ----------------------
     // Activations: wave v, load i fills LDS bytes 1024*(4v+i) .. +1023, i.e.
     // rows 16v + 4i + l/16; lane l fills position l%16 of its row, which holds
     // chunk (l%16) ^ (row%16) (eight bf16, k = 8*chunk + 0..7).
-    // Chunks past K (last k-tile of a ragged K) are pointed past the buffer
-    // end as well, so they land as zeros.
-    uint32_t xoff[4];
-    int xk[4];                                             // k of the chunk within a k-tile
+    // k-tile c is at xoff + 256c; the last k-tile of a ragged K uses xlast,
+    // which points chunks past K outside the buffer as well.
+    const bool ragged = (K & 127) != 0;
+    uint32_t xoff[4], xlast[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int row = m0 + 16 * wave + 4 * i + (lane >> 4);
         const int chunk = (lane & 15) ^ ((4 * i + (lane >> 4)) & 15);
-        xk[i] = 8 * chunk;
         xoff[i] = row < M ? (uint32_t)(((int64_t)row * K + 8 * chunk) * 2) : kOutside;
+        xlast[i] = row < M && 128 * (KT - 1) + 8 * chunk < K
+                       ? xoff[i] + 256u * (uint32_t)(KT - 1) : kOutside;
     }
     // Weights: chunk e = 64*(8q + v) + lane for wave v's q-th load; e < 64*TT:
     // code tile e/64, slot e%64; else scale tile (e-64TT)/8, part (e-64TT)%8.
@@ -172,20 +175,23 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         wlds[q] = 64 * (8 * q + wave) < kWChunks ? 1024 * (8 * q + wave) : kWDataBytes;
     }
 
-    // One stage load n (0..3 activations, then weights) of k-tile c; adv is
-    // the byte advance of k-tile c (or kSkip, which puts every lane past the
-    // buffer end so the load only writes zeros into a free stage).
+    // One stage load n (0..3 activations, then weights) of k-tile c.  A load
+    // that is not live (past the last k-tile) gets a buffer of size 0 and
+    // only writes zeros into a free stage.
     constexpr int kLoads = 4 + kWLoadsPerWave;
     auto issue_load = [&](int n, int c, bool live, uint8_t *sx, uint8_t *sw) __attribute__((always_inline)) {
         if (n < 4) {
             const int i = n < 4 ? n : 0;
-            const uint32_t adv = live ? 256u * c : kSkip;
-            load_lds16(rx, sx + 1024 * (4 * wave + n), 128 * c + xk[i] < K ? xoff[i] + adv : kOutside);
+            const bool last = ragged && c == KT - 1;
+            load_lds16(make_rsrc(x, live ? xbytes : 0u), sx + 1024 * (4 * wave + n),
+                       last ? xlast[i] : xoff[i], last ? 0u : 256u * (uint32_t)c);
         } else {
-            const int q = n - 4;
+            const int q = n - 4 < kWLoadsPerWave ? n - 4 : 0;
             const bool code = 8 * q + wave < TT;
-            const uint32_t adv = live ? (code ? (uint32_t)kTileCodeBytes : (uint32_t)kTileScaleBytes) * c : kSkip;
-            load_lds16(code ? rc : rs, sw + wlds[q], woff[q] + adv);
+            const uint8_t *base = code ? pcodes : pscales;
+            const uint32_t bytes = live ? (code ? cbytes : sbytes) : 0u;
+            load_lds16(make_rsrc(base, bytes), sw + wlds[q], woff[q],
+                       (code ? (uint32_t)kTileCodeBytes : (uint32_t)kTileScaleBytes) * (uint32_t)c);
         }
     };
     auto issue_stage = [&](int c, bool live, uint8_t *sx, uint8_t *sw) __attribute__((always_inline)) {
@@ -195,7 +201,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     };
 
     // ---- accumulators -------------------------------------------------------
-    // accF[j][i]: whole tile w*Q + j, row block (rb + i) & 7.
+    // accF[j][i]: whole tile w*Q + j, row block i ^ rb.
     // accR[j][i]: remaining tile, row block rb + i.
     floatx4_t accF[Q > 0 ? Q : 1][8];
     floatx4_t accR[RB > 0 ? RB : 1][RR];
@@ -217,90 +223,27 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     const int code_lane = (32 * h + r) * 16 + kh * 8;
     const int scale_lane = r * 8 + kh * 4;
     const int a_lane = r * 256;
-
-    // ---- one k-tile per barrier (variants with four whole tiles per wave) ----
-    // Without double-buffered operands, for register room: after the barrier
-    // the wave reads its words, dequantises a k-step's operands and runs its
-    // MFMAs, twice.
-    auto compute = [&](int c, uint8_t *sx, const uint8_t *sw, uint8_t *sxn, uint8_t *swn) __attribute__((always_inline)) {
-        // wait for this stage (the next one may still be in flight), then
-        // make every wave's loads of it visible; this wave's LDS reads of the
-        // stage that is overwritten next are complete (lgkmcnt(0))
-        wait_vm(4 + kWLoadsPerWave);
-        __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        // the loads of k-tile c+2 (into the stage consumed at c-1) are spread
-        // over this k-tile's MFMAs: issued in one burst they stall the wave
-        // until the memory pipeline accepts them
-        const bool live = c + 2 < KT;
-        // code bytes of this wave's blocks 4kh..4kh+3 from the two slots, and
-        // their scales (shifted so block 4kh + 2dd + gq/2 sits in byte 2dd)
-        uint2 pF[Q > 0 ? Q : 1], qF[Q > 0 ? Q : 1], pR[RB > 0 ? RB : 1], qR[RB > 0 ? RB : 1];
-        uint32_t sF[Q > 0 ? Q : 1], sR[RB > 0 ? RB : 1];
+    // The wave visits row blocks i ^ rb, i = 0..7 (rb is even, a multiple of
+    // 4 when RT = 2): the activation operand of row block i ^ rb at step
+    // base ab is at ab + ((i ^ rb) << 12), i.e. a few per-step base
+    // addresses plus constant offsets.
+    auto row_bases = [&](const uint8_t *ab, const uint8_t **rbase) __attribute__((always_inline)) {
+        if (RT == 0) {
+            rbase[0] = ab;
+        } else if (RT == 2) {
+            rbase[0] = ab + (rb << 12);                    // i = 0..3: rows rb + i
+            rbase[1] = ab + ((4 - rb) << 12);              // i = 4..7: rows (4 - rb) + i - 4
+        } else {
 #pragma unroll
-        for (int j = 0; j < Q + RB; ++j) {
-            const int jt = j < Q ? w * Q + j : (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + (j - Q));
-            const uint8_t *cb = sw + jt * kTileCodeBytes + code_lane;
-            const uint2 p = *reinterpret_cast<const uint2 *>(cb);
-            const uint2 q = *reinterpret_cast<const uint2 *>(cb + 256);
-            const uint32_t sv = *reinterpret_cast<const uint32_t *>(
-                                    sw + TT * kTileCodeBytes + jt * kTileScaleBytes + scale_lane) >> (8 * (gq >> 1));
-            if (j < Q) {
-                pF[j] = p; qF[j] = q; sF[j] = sv;
-            } else {
-                pR[j - Q] = p; qR[j - Q] = q; sR[j - Q] = sv;
-            }
-        }
-
-#pragma unroll
-        for (int dd = 0; dd < 2; ++dd) {
-            const int d = 2 * kh + dd;
-            // B operands of every tile for this step, then one A operand at a
-            // time (fewer live registers than holding all eight)
-            bf16x8_t bF[Q > 0 ? Q : 1], bR[RB > 0 ? RB : 1];
-#pragma unroll
-            for (int j = 0; j < Q; ++j) {
-                const uint32_t wd = __builtin_amdgcn_perm(dd ? qF[j].y : qF[j].x, dd ? pF[j].y : pF[j].x, sel);
-                bF[j] = dequant8(wd, dd ? e4m3_to_f32<2>(sF[j]) : e4m3_to_f32<0>(sF[j]));
-            }
-#pragma unroll
-            for (int j = 0; j < RB; ++j) {
-                const uint32_t wd = __builtin_amdgcn_perm(dd ? qR[j].y : qR[j].x, dd ? pR[j].y : pR[j].x, sel);
-                bR[j] = dequant8(wd, dd ? e4m3_to_f32<2>(sR[j]) : e4m3_to_f32<0>(sR[j]));
-            }
-            const uint8_t *ab = sx + a_lane + (((4 * d + gq) ^ r) << 4);
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                if ((8 * dd + i) % 2 == 0 && (8 * dd + i) / 2 < kLoads)
-                    issue_load((8 * dd + i) / 2, c + 2, live, sxn, swn);
-                const int mt = (rb + i) & 7;
-                const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(ab + mt * 4096);
-#pragma unroll
-                for (int j = 0; j < Q; ++j)
-                    accF[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bF[j], accF[j][i], 0, 0, 0);
-                if (i < RR) {
-#pragma unroll
-                    for (int j = 0; j < RB; ++j)
-                        accR[j][i < RR ? i : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            a, bR[j], accR[j][i < RR ? i : 0], 0, 0, 0);
-                }
-            }
+            for (int k = 0; k < 4; ++k)                    // i = 2k, 2k+1: rows (2k ^ rb) + i % 2
+                rbase[k] = ab + (((2 * k) ^ rb) << 12);
         }
     };
-
-    auto run_single = [&]() __attribute__((always_inline)) {
-    // stages 0, 1 in flight, then one k-tile per step (every k-tile c issues
-    // the loads of c+2, skipped ones included, so the wait at k-tile c always
-    // leaves exactly one stage of loads in flight)
-    issue_stage(0, true, sx0, sw0);
-    issue_stage(1, KT > 1, sx1, sw1);
-    for (int c = 0; c < KT; c += 3) {
-        compute(c, sx0, sw0, sx2, sw2);
-        if (c + 1 < KT)
-            compute(c + 1, sx1, sw1, sx0, sw0);
-        if (c + 2 < KT)
-            compute(c + 2, sx2, sw2, sx1, sw1);
-    }
+    auto row_operand = [&](const uint8_t *const *rbase, int i) __attribute__((always_inline)) {
+        const uint8_t *pa = RT == 0 ? rbase[0] + (i << 12)
+                          : RT == 2 ? rbase[i >> 2] + ((i & 3) << 12)
+                                    : rbase[i >> 1] + ((i & 1) << 12);
+        return *reinterpret_cast<const bf16x8_t *>(pa);
     };
 
     // ---- software-pipelined k-loop --------------------------------------------
@@ -332,11 +275,11 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     // operands b; fill(i) is independent work placed after row block i
     auto mfma_step = [&](int dd, const uint8_t *sx, const bf16x8_t *b, auto fill) __attribute__((always_inline)) {
         const int d = 2 * kh + dd;
-        const uint8_t *ab = sx + a_lane + (((4 * d + gq) ^ r) << 4);
+        const uint8_t *rbase[4];
+        row_bases(sx + a_lane + (((4 * d + gq) ^ r) << 4), rbase);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            const int mt = (rb + i) & 7;
-            const bf16x8_t a = *reinterpret_cast<const bf16x8_t *>(ab + mt * 4096);
+            const bf16x8_t a = row_operand(rbase, i);
 #pragma unroll
             for (int j = 0; j < Q; ++j)
                 accF[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], accF[j][i], 0, 0, 0);
@@ -362,8 +305,8 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
             if (i < NB)
                 b1[i < NB ? i : 0] = dequant_tile(i < NB ? i : 0, 1);
         });
-        wait_vm(0);
-        __builtin_amdgcn_s_waitcnt(0xc07f);                 // lgkmcnt(0)
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                 // lgkmcnt(0)
         __builtin_amdgcn_s_barrier();
         const bool live = c + 2 < KT;
         mfma_step(1, sxc, b1, [&](int i) __attribute__((always_inline)) {
@@ -378,13 +321,12 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         static_assert(NB <= 6, "every tile is dequantised inside the row loop");
     };
 
-    auto run_pipelined = [&]() __attribute__((always_inline)) {
     // stages 0 and 1 (skipped past the last k-tile) land before the loop;
     // afterwards every k-tile issues the loads of the k-tile two ahead
     issue_stage(0, true, sx0, sw0);
     issue_stage(1, KT > 1, sx1, sw1);
-    wait_vm(0);
-    __builtin_amdgcn_s_waitcnt(0xc07f);
+    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
     for (int j = 0; j < NB; ++j) {
@@ -398,22 +340,15 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         if (c + 2 < KT)
             ktile(c + 2, sx2, sw0, sx1, sw1);
     }
-    };
 
-    // Double-buffered operands need about 40 more registers than fit beside
-    // the accumulators of four whole tiles.
-    if constexpr (Q >= 4)
-        run_single();
-    else
-        run_pipelined();
 
     // ---- add the k-halves: waves 4..7 hand their sums to waves 0..3 --------
     {
         // every wave is past its last LDS read of the stages (the last
         // compute ended with them) and its trailing zero-writing loads have
         // landed, so the stage buffers are free
-        wait_vm(0);
-        __builtin_amdgcn_s_waitcnt(0xc07f);
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
         constexpr int kAcc = 8 * Q + RB * RR;                // floatx4 per lane
         // one slot per wave pair: three activation stages and one weight
@@ -429,7 +364,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
                 for (int f = p0; f < kAcc && f < p0 + kPass; ++f)
                     red[(f - p0) * 64 + lane] = f < 8 * Q ? accF[f >> 3][f & 7] : accR[(f - 8 * Q) / RR][(f - 8 * Q) % RR];
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
             __builtin_amdgcn_s_barrier();
             if (kh == 0) {
 #pragma unroll
@@ -440,7 +375,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
                         accR[(f - 8 * Q) / RR][(f - 8 * Q) % RR] += red[(f - p0) * 64 + lane];
                 }
             }
-            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
             __builtin_amdgcn_s_barrier();
         }
         if (kh == 1)
@@ -455,7 +390,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         if (t < NT && n < N) {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const int mt = (rb + i) & 7;
+                const int mt = i ^ rb;
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const int m = m0 + 16 * mt + 4 * gq + e;
