@@ -10,7 +10,10 @@ with gcc into ``liboracle.so`` and exposes numpy-level wrappers:
 * :func:`e2m1`, :func:`e4m3`, :func:`bf16` — element decoders (closed forms),
 * :func:`dequant_row` — one weight row in fp64,
 * :func:`proj` / :func:`proj_rows` — y and the tolerance base S in fp64,
-* :func:`check` — the acceptance test |y_gpu - y_ref| <= rtol * S.
+* :func:`check` — the acceptance test |y_gpu - y_ref| <= rtol * S,
+* :func:`silu_mul_cols` / :func:`check_bf16` — the fused gate/up projection
+  h = silu(gate) * up on a weight whose gate and up rows are interleaved in
+  groups of 16, its error allowance, and the bf16 acceptance test.
 
 Formats and layouts are documented at the top of ``oracle.c``.
 """
@@ -66,6 +69,12 @@ def load(path: str = LIB):
     lib.orc_proj.restype = ctypes.c_int
     lib.orc_check.argtypes = [i64, vp, vp, vp, dbl, ctypes.POINTER(dbl)]
     lib.orc_check.restype = i64
+    lib.orc_silu_mul.argtypes = [i64, vp, vp, vp]
+    lib.orc_silu_mul.restype = None
+    lib.orc_silu_mul_bound.argtypes = [i64, vp, vp, vp, vp, dbl, vp]
+    lib.orc_silu_mul_bound.restype = None
+    lib.orc_check_bf16.argtypes = [i64, vp, vp, vp, ctypes.POINTER(dbl)]
+    lib.orc_check_bf16.restype = i64
     if path == LIB:
         _lib = lib
     return lib
@@ -148,4 +157,53 @@ def check(y_ref, S, y_gpu, rtol: float = RTOL, lib=None):
     worst = ctypes.c_double(0.0)
     bad = (lib or load()).orc_check(yr.size, _ptr(yr), _ptr(ss), _ptr(yg), float(rtol),
                                     ctypes.byref(worst))
+    return int(bad), float(worst.value)
+
+
+# ---- fused gate/up + silu(gate) * up --------------------------------------
+
+def gate_up_rows(F: int):
+    """Rows of the fused [2F][K] weight holding gate row f and up row f
+    (interleaved in groups of 16: gate rows 16p.. at 32p.., up rows 16 later)."""
+    f = np.arange(F, dtype=np.int64)
+    gate = 32 * (f // 16) + f % 16
+    return gate, gate + 16
+
+
+def silu_mul(gate, up, lib=None) -> np.ndarray:
+    """h = silu(gate) * up in fp64, elementwise."""
+    a = np.ascontiguousarray(gate, dtype=np.float64)
+    b = np.ascontiguousarray(up, dtype=np.float64)
+    assert a.shape == b.shape
+    h = np.empty_like(a)
+    (lib or load()).orc_silu_mul(a.size, _ptr(a), _ptr(b), _ptr(h))
+    return h
+
+
+def silu_mul_cols(codes, scales, g: float, x, F: int, cols=None, nthreads=None, lib=None):
+    """h[M][len(cols)] = silu(gate) * up in fp64 for output columns `cols` of
+    the fused projection (codes/scales of the interleaved [2F][K] weight), and
+    the allowance bound[M][len(cols)] of the fp32 path before its bf16
+    rounding.  cols=None evaluates every column."""
+    lib = lib or load()
+    grow, urow = gate_up_rows(F)
+    if cols is not None:
+        c = np.asarray(cols, dtype=np.int64)
+        grow, urow = grow[c], urow[c]
+    a, Sa = proj_rows(codes, scales, g, x, grow, nthreads, lib)
+    b, Sb = proj_rows(codes, scales, g, x, urow, nthreads, lib)
+    h = silu_mul(a, b, lib)
+    bound = np.empty_like(h)
+    lib.orc_silu_mul_bound(h.size, _ptr(a), _ptr(b), _ptr(Sa), _ptr(Sb), float(RTOL), _ptr(bound))
+    return h, bound
+
+
+def check_bf16(h_ref, bound, h_gpu_bits, lib=None):
+    """Returns (number of failing elements, max |h-h_ref| / allowance)."""
+    hr = np.ascontiguousarray(h_ref, dtype=np.float64)
+    bd = np.ascontiguousarray(bound, dtype=np.float64)
+    hg = np.ascontiguousarray(h_gpu_bits, dtype=np.uint16)
+    assert hr.shape == bd.shape == hg.shape, (hr.shape, bd.shape, hg.shape)
+    worst = ctypes.c_double(0.0)
+    bad = (lib or load()).orc_check_bf16(hr.size, _ptr(hr), _ptr(bd), _ptr(hg), ctypes.byref(worst))
     return int(bad), float(worst.value)

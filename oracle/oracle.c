@@ -249,3 +249,78 @@ int64_t orc_check(int64_t count, const double *yref, const double *S,
         *max_ratio = worst;
     return bad;
 }
+
+/* ---- fused gate/up: h = silu(gate) * up ---------------------------------
+ *
+ * The FlashRT "Qwen3.6 NVFP4 usage" page, environment table (the fused MLP
+ * gate/up and fused silu(gate)*up entries): when gate and up share one global
+ * scale they run as one NVFP4 projection, followed by silu(gate) * up, with
+ * silu(z) = z * sigmoid(z) = z / (1 + exp(-z)) (the SwiGLU gate).
+ *
+ * This library's fused weight (a reading; the page gives no layout) stacks
+ * gate and up rows interleaved in groups of 16: rows 32p..32p+15 are gate rows
+ * 16p..16p+15 and rows 32p+16..32p+31 are up rows 16p..16p+15, so gate row f
+ * sits at 32*(f/16) + f%16 and up row f 16 rows later.  The row selection is
+ * done by the Python wrapper; this file supplies the fp64 arithmetic.
+ */
+void orc_silu_mul(int64_t count, const double *gate, const double *up, double *h)
+{
+    for (int64_t i = 0; i < count; ++i)
+        h[i] = gate[i] / (1.0 + exp(-gate[i])) * up[i];
+}
+
+/*
+ * Error bound for h computed from gate' = gate + da and up' = up + db with
+ * |da| <= rtol*Sg, |db| <= rtol*Su (the projection's acceptance test):
+ *   |silu(gate') up' - silu(gate) up|
+ *       <= max|silu'| |da| (|up| + |db|) + |silu(gate)| |db|,
+ * and max over z of |silu'(z)| = |sigmoid(z) (1 + z (1 - sigmoid(z)))| is
+ * 1.0998 (at z ~ 2.40), taken as 1.1.  The bf16 rounding of the result is
+ * added by orc_check_bf16.
+ */
+void orc_silu_mul_bound(int64_t count, const double *gate, const double *up, const double *Sg,
+                        const double *Su, double rtol, double *bound)
+{
+    for (int64_t i = 0; i < count; ++i) {
+        double da = rtol * Sg[i], db = rtol * Su[i];
+        double sg = gate[i] / (1.0 + exp(-gate[i]));
+        bound[i] = 1.1 * da * (fabs(up[i]) + db) + fabs(sg) * db;
+    }
+}
+
+/*
+ * Acceptance test of bf16 results (bit patterns) against fp64 references:
+ *   |h_gpu - h_ref| <= bound + 2^-8 (|h_ref| + bound),
+ * the second term covering the round-to-nearest-even to bf16 (relative error
+ * at most 2^-9) and the fp32 arithmetic before it.  A NaN h_ref requires a
+ * NaN h_gpu; a finite h_ref requires a finite h_gpu.  Returns the number of
+ * failing elements; *max_ratio receives the largest |h_gpu - h_ref| over its
+ * allowance (diagnostic).
+ */
+int64_t orc_check_bf16(int64_t count, const double *href, const double *bound,
+                       const uint16_t *hgpu, double *max_ratio)
+{
+    int64_t bad = 0;
+    double worst = 0.0;
+    for (int64_t i = 0; i < count; ++i) {
+        double r = href[i], v = orc_bf16(hgpu[i]);
+        if (isnan(r)) {
+            if (!isnan(v))
+                ++bad;
+            continue;
+        }
+        if (!isfinite(v)) {
+            ++bad;
+            continue;
+        }
+        double allow = bound[i] + ldexp(fabs(r) + bound[i], -8);
+        double d = fabs(v - r);
+        if (allow > 0.0 && d / allow > worst)
+            worst = d / allow;
+        if (d > allow)
+            ++bad;
+    }
+    if (max_ratio)
+        *max_ratio = worst;
+    return bad;
+}

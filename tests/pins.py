@@ -303,6 +303,89 @@ def pin_synth_roundtrip(lib):
         assert (np.abs(w[n] - d) <= 1.0 * s + 1e-12).all()
 
 
+# ---- fused gate/up + silu(gate) * up --------------------------------------
+
+def pin_silu_mul_torch(lib):
+    """silu(gate) * up against torch.nn.functional.silu (a library routine) in
+    fp64, over magnitudes from 1e-6 to 800 of both signs, and two closed
+    forms: silu(0) = 0 and silu(1) = 1 / (1 + 1/e)."""
+    rng = np.random.default_rng(5)
+    mag = 10.0 ** rng.uniform(-6, np.log10(800.0), 4000)
+    gate = mag * rng.choice([-1.0, 1.0], mag.size)
+    up = rng.normal(0.0, 3.0, gate.size)
+    h = oracle.silu_mul(gate, up, lib)
+    ref = (torch.nn.functional.silu(torch.from_numpy(gate)) * torch.from_numpy(up)).numpy()
+    assert np.allclose(h, ref, rtol=1e-14, atol=1e-300), np.max(np.abs(h - ref))
+    h0 = oracle.silu_mul(np.array([0.0, 1.0, -1.0]), np.array([7.0, 1.0, 1.0]), lib)
+    assert h0[0] == 0.0
+    assert abs(h0[1] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert abs(h0[2] + 1.0 / (1.0 + math.e)) < 1e-15
+
+
+def _interleave16(gate, up):
+    """Stack [F][W] gate and up row blocks as the fused weight: groups of 16
+    gate rows then 16 up rows (F a multiple of 16)."""
+    F, W = gate.shape
+    return np.stack([gate.reshape(F // 16, 16, W), up.reshape(F // 16, 16, W)], axis=1).reshape(2 * F, W)
+
+
+def pin_silu_mul_fused_rows(lib):
+    """The fused projection's row selection: separate gate and up matrices,
+    interleaved here with a reshape, projected by the fused path, against the
+    plain projections of the separate matrices and torch's silu."""
+    F, K, M = 48, 96, 3
+    mg = synth.nvfp4_normal_matrix(81, 1, F, K, threads=1)
+    mu = synth.nvfp4_normal_matrix(81, 2, F, K, threads=1)
+    x = synth.x_bf16(81, 3, M, K, threads=1)
+    codes = _interleave16(mg.codes, mu.codes)
+    scales = _interleave16(mg.scales, mu.scales)
+    g = 0.75                                       # one global scale for both halves
+    h, _ = oracle.silu_mul_cols(codes, scales, g, x, F, lib=lib)
+    a, _ = oracle.proj(mg.codes, mg.scales, g, x, lib=lib)
+    b, _ = oracle.proj(mu.codes, mu.scales, g, x, lib=lib)
+    ref = (torch.nn.functional.silu(torch.from_numpy(a)) * torch.from_numpy(b)).numpy()
+    assert np.allclose(h, ref, rtol=1e-13, atol=1e-300)
+    cols = np.array([0, 15, 16, 47])
+    hc, _ = oracle.silu_mul_cols(codes, scales, g, x, F, cols=cols, lib=lib)
+    assert np.array_equal(hc, h[:, cols])
+
+
+def pin_silu_mul_bound(lib):
+    """The allowance: max |silu'| over a fine grid stays below the 1.1 the
+    bound uses; a bound-sized perturbation of gate and up moves h by no more
+    than the bound; and the bf16 acceptance test passes a correctly rounded
+    value and fails one an allowance away."""
+    z = torch.linspace(-40.0, 40.0, 800001, dtype=torch.float64, requires_grad=True)
+    torch.nn.functional.silu(z).sum().backward()
+    assert z.grad.abs().max().item() < 1.1
+    rng = np.random.default_rng(6)
+    a = rng.normal(0, 4, 2000)
+    b = rng.normal(0, 4, 2000)
+    Sa = np.abs(a) * rng.uniform(1, 50, a.size)
+    Sb = np.abs(b) * rng.uniform(1, 50, b.size)
+    bound = np.empty(a.size)
+    lib.orc_silu_mul_bound(a.size, a.ctypes.data, b.ctypes.data, Sa.ctypes.data, Sb.ctypes.data,
+                           oracle.RTOL, bound.ctypes.data)
+    for sa in (-1, 1):
+        for sb in (-1, 1):
+            a2 = a + sa * oracle.RTOL * Sa
+            b2 = b + sb * oracle.RTOL * Sb
+            moved = np.abs(oracle.silu_mul(a2, b2, lib) - oracle.silu_mul(a, b, lib))
+            assert (moved <= bound * (1 + 1e-12)).all()
+    href = np.array([1.0, -3.0, 0.0, np.nan, 100.0])
+    bd = np.array([0.0, 0.01, 0.0, 0.0, 0.5])
+    ok = torch.tensor([1.0, -3.0078125, 0.0, float("nan"), 100.5], dtype=torch.bfloat16)
+    bits = ok.view(torch.int16).numpy().view(np.uint16)
+    bad, _ = oracle.check_bf16(href, bd, bits, lib)
+    assert bad == 0, bad
+    for i, v in [(0, 1.0078125 * 1.0078125), (2, 1e-30), (3, 1.0), (4, 102.0)]:
+        t = ok.clone()
+        t[i] = v
+        bad, _ = oracle.check_bf16(href, bd, t.view(torch.int16).numpy().view(np.uint16), lib)
+        assert bad == 1, (i, v, bad)
+
+
 ALL_PINS = [pin_e2m1_table, pin_e4m3_torch, pin_e4m3_landmarks, pin_bf16_torch,
             pin_dequant_rows, pin_exact_tiny_fast, pin_abs_sum, pin_one_hot,
-            pin_invariants, pin_nan_scale, pin_check]
+            pin_invariants, pin_nan_scale, pin_check, pin_silu_mul_torch,
+            pin_silu_mul_fused_rows, pin_silu_mul_bound]

@@ -39,6 +39,15 @@ MUTANTS = {
     "check_signed_diff": ("double d = fabs(v - r);", "double d = v - r;", 1),
     "check_zero_base": ("if (v != 0.0)\n                ++bad;", "if (0)\n                ++bad;", 1),
     "check_nan": ("if (!isnan(v))\n                ++bad;", "if (0)\n                ++bad;", 1),
+    "silu_sign": ("h[i] = gate[i] / (1.0 + exp(-gate[i])) * up[i];",
+                  "h[i] = gate[i] / (1.0 + exp(gate[i])) * up[i];", 1),
+    "silu_swapped": ("h[i] = gate[i] / (1.0 + exp(-gate[i])) * up[i];",
+                     "h[i] = up[i] / (1.0 + exp(-up[i])) * gate[i];", 1),
+    "silu_sigmoid_only": ("h[i] = gate[i] / (1.0 + exp(-gate[i])) * up[i];",
+                          "h[i] = 1.0 / (1.0 + exp(-gate[i])) * up[i];", 1),
+    "silu_bound_slope": ("bound[i] = 1.1 * da", "bound[i] = 0.5 * da", 1),
+    "silu_bound_up_term": ("+ fabs(sg) * db;", ";", 1),
+    "check_bf16_rounding": ("ldexp(fabs(r) + bound[i], -8)", "ldexp(fabs(r) + bound[i], -4)", 1),
 }
 
 
