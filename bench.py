@@ -20,6 +20,10 @@ Also measured and reported in the same JSON line:
                 `traffic` (HBM bytes per launch, mean of the two) from the
                 rocprofv3 counter summary in profiles/ when current.
   shapes        the other workloads' GEMVs (M = 7 verify, lm-head, 4B shapes).
+  fused_gate_up the MLP's gate and up weights as one fused 2F x K NVFP4 GEMV
+                with the silu(gate)*up epilogue (bf16 out), F = 17408, K = 5120,
+                at M = 1 and M = 7, beside the plain GEMV over the same packed
+                weight (fp32 out, no epilogue).
   pack          the one-time weight swizzle (read + write bytes / s).
   cpu_baseline  the CPU oracle on the decode step, on the host cores.
 """
@@ -104,7 +108,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="wall-time bound of the cpu_baseline sample")
-    ap.add_argument("--only", choices=["dec", "pre", "all"], default="all",
+    ap.add_argument("--only", choices=["dec", "pre", "mlp", "all"], default="all",
                     help="restrict the run (for profiling one kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
@@ -265,6 +269,43 @@ def main():
         out["pack"] = {"N": lm.N, "K": lm.K, "us": round(ms * 1e3, 1),
                        "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
         del codes, scales, pc, ps
+
+    # ---- fused gate/up + silu(gate)*up ------------------------------------
+    if args.only in ("mlp", "all"):
+        (c,) = synth.workload_cases("mlp")
+        F, K = c.N // 2, c.K
+        fused = {}
+        for M in (1, 7):
+            cm = synth.Case("mlp", c.name, M, c.matrix,
+                            c.x if M == 1 else synth.x_bf16(5, 10 + M, M, K))
+            b_plain = algo_bytes(M, 2 * F, K)
+            u = upload(cm, copies_for(b_plain))
+            h = torch.empty((M, F), dtype=torch.int16, device=dev)
+            ws = torch.zeros(q4.q4proj_silu_mul_workspace_bytes(M, F, K), dtype=torch.uint8,
+                             device=dev)
+
+            def fused_launch(i, u=u, h=h, ws=ws, M=M):
+                pc, ps = u["w"][i % len(u["w"])]
+                return lambda: q4.q4proj_gemv_silu_mul(pc, ps, u["g"], u["x"], h, M, F, K,
+                                                       workspace=ws)
+
+            n = max(10, args.steps // 4)
+            for i in range(3):
+                fused_launch(i)()
+                launcher("gemv", u, i)()
+            ms_f, _ = timed_region(torch, [fused_launch(i) for i in range(n)], n)
+            ms_p, _ = timed_region(torch, [launcher("gemv", u, i) for i in range(n)], n)
+            b_fused = 2 * F * K // 2 + 2 * F * K // 16 + 2 * M * K + 2 * M * F + 4
+            fused[f"M={M}"] = {
+                "M": M, "F": F, "K": K, "us": round(ms_f * 1e3, 2),
+                "gbs": round(b_fused / (ms_f * 1e-3) / 1e9, 1),
+                "hbm_frac": round(b_fused / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                "plain_gemv_2F_us": round(ms_p * 1e3, 2)}
+            del u, h, ws
+        out["fused_gate_up"] = {
+            "workload": "fused gate/up 5120 -> 2x17408 NVFP4 GEMV + silu(gate)*up -> bf16",
+            "kernel": "gemv_sk_kernel<ROWS, 4, false, true>", "per_M": fused,
+            "kernel_source_sha256_16": src_digest("q4p_gemv.hip")}
 
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -46,6 +46,10 @@ _lib.q4proj_gemv.argtypes = _PROJ_ARGS
 _lib.q4proj_gemv.restype = ctypes.c_int
 _lib.q4proj_gemm.argtypes = _PROJ_ARGS
 _lib.q4proj_gemm.restype = ctypes.c_int
+_lib.q4proj_silu_mul_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.q4proj_silu_mul_workspace_bytes.restype = _sz
+_lib.q4proj_gemv_silu_mul.argtypes = _PROJ_ARGS
+_lib.q4proj_gemv_silu_mul.restype = ctypes.c_int
 _lib.q4proj_status_string.argtypes = [ctypes.c_int]
 _lib.q4proj_status_string.restype = ctypes.c_char_p
 _lib.q4proj_last_hip_error.argtypes = []
@@ -54,6 +58,7 @@ _lib.q4proj_last_hip_error.restype = ctypes.c_char_p
 #: Exported symbols declared by include/q4proj.h.
 SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
            "q4proj_pack", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
+           "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul",
            "q4proj_status_string", "q4proj_last_hip_error")
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE, EWORKSPACE, EHIP = range(6)
@@ -89,6 +94,10 @@ def q4proj_packed_scales_bytes(N: int, K: int) -> int:
 
 def q4proj_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(_lib.q4proj_workspace_bytes(M, N, K))
+
+
+def q4proj_silu_mul_workspace_bytes(M: int, F: int, K: int) -> int:
+    return int(_lib.q4proj_silu_mul_workspace_bytes(M, F, K))
 
 
 def _stream(t: torch.Tensor, stream):
@@ -155,14 +164,20 @@ def default_workspace(device, nbytes: int):
     return ws
 
 
+def _bf16_bits(t, name):
+    """A bfloat16 tensor as its 16-bit patterns (a view); int16/uint16 pass."""
+    if isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16:
+        t = t.view(torch.int16)
+    if not isinstance(t, torch.Tensor) or t.dtype not in (torch.int16, torch.uint16):
+        raise TypeError(f"{name} must hold bf16 (bfloat16 or 16-bit bit patterns)")
+    return t
+
+
 def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, workspace, stream):
     dev = x.device
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
-    if x.dtype == torch.bfloat16:
-        x = x.view(torch.int16)
-    if x.dtype not in (torch.int16, torch.uint16):
-        raise TypeError(f"x must hold bf16 (bfloat16 or 16-bit bit patterns), got {x.dtype}")
+    x = _bf16_bits(x, "x")
     _need(x, "x", x.dtype, M * K, dev)
     _need(y, "y", torch.float32, M * N, dev)
     ws_ptr, ws_bytes = None, 0
@@ -189,6 +204,31 @@ def q4proj_gemm(packed_codes, packed_scales, global_scale: float, x, y, M: int, 
     """y[M][N] fp32 = x[M][K] bf16 . dequant(W)^T for any M >= 1."""
     _proj(_lib.q4proj_gemm, "q4proj_gemm", packed_codes, packed_scales, global_scale, x, y, M, N,
           K, workspace, stream)
+
+
+def q4proj_gemv_silu_mul(packed_codes, packed_scales, global_scale: float, x, h, M: int, F: int,
+                         K: int, workspace=None, stream=None) -> None:
+    """h[M][F] bf16 = silu(gate) * up of the fused [2F][K] gate/up weight
+    (16-row gate and up blocks alternating), 1 <= M <= 16."""
+    dev = x.device
+    N = 2 * F
+    _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
+    _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
+    x = _bf16_bits(x, "x")
+    h = _bf16_bits(h, "h")
+    _need(x, "x", x.dtype, M * K, dev)
+    _need(h, "h", h.dtype, M * F, dev)
+    ws_ptr, ws_bytes = None, 0
+    if workspace is None:
+        workspace = default_workspace(dev, q4proj_silu_mul_workspace_bytes(M, F, K))
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    with torch.cuda.device(dev):
+        _check(_lib.q4proj_gemv_silu_mul(packed_codes.data_ptr(), packed_scales.data_ptr(),
+                                         float(global_scale), x.data_ptr(), h.data_ptr(), M, F, K,
+                                         ws_ptr, ws_bytes, _stream(x, stream)),
+               "q4proj_gemv_silu_mul")
 
 
 def pack_weight(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, stream=None):

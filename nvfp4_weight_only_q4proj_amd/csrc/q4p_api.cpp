@@ -178,6 +178,53 @@ q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_sca
                                        workspace, static_cast<hipStream_t>(stream)));
 }
 
+size_t q4proj_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K)
+{
+    if (M <= 0 || M > Q4PROJ_GEMV_MAX_M || F <= 0 || F % 16 != 0 || F > ((int64_t)1 << 29) ||
+        !shape_ok(2 * F, K))
+        return 0;
+    return q4p::gemv_silu_mul_workspace_bytes(M, F, K);
+}
+
+q4proj_status q4proj_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                   float global_scale, const uint16_t *x, uint16_t *h, int64_t M,
+                                   int64_t F, int64_t K, void *workspace, size_t workspace_bytes,
+                                   void *stream)
+{
+    if (!packed_codes || !packed_scales || !x || !h)
+        return Q4P_EINVAL;
+    if (M <= 0 || M > (int64_t)1 << 24 || F <= 0 || F % 16 != 0 || F > ((int64_t)1 << 29) ||
+        !shape_ok(2 * F, K))
+        return Q4P_EINVAL;
+    if (!aligned(packed_codes, 16) || !aligned(packed_scales, 8) || !aligned(x, 16) ||
+        !aligned(h, 2))
+        return Q4P_EINVAL;
+    const int64_t N = 2 * F;
+    const size_t hbytes = (size_t)M * (size_t)F * 2, xbytes = (size_t)M * (size_t)K * 2;
+    const size_t pcb = q4proj_packed_codes_bytes(N, K), psb = q4proj_packed_scales_bytes(N, K);
+    if (overlap(h, hbytes, x, xbytes) || overlap(h, hbytes, packed_codes, pcb) ||
+        overlap(h, hbytes, packed_scales, psb))
+        return Q4P_EINVAL;
+    if (M > Q4PROJ_GEMV_MAX_M)
+        return Q4P_EUNSUPPORTED;
+    const size_t need = q4proj_silu_mul_workspace_bytes(M, F, K);
+    if (need == 0)
+        return Q4P_EUNSUPPORTED;
+    if (workspace_bytes < need)
+        return Q4P_EWORKSPACE;
+    if (!workspace || !aligned(workspace, 8))
+        return Q4P_EINVAL;
+    if (overlap(workspace, need, h, hbytes) || overlap(workspace, need, x, xbytes) ||
+        overlap(workspace, need, packed_codes, pcb) || overlap(workspace, need, packed_scales, psb))
+        return Q4P_EINVAL;
+    q4proj_status st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_gemv_silu_mul(packed_codes, packed_scales, global_scale, x, h,
+                                                M, F, K, workspace,
+                                                static_cast<hipStream_t>(stream)));
+}
+
 q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
                           float global_scale, const uint16_t *x, float *y, int64_t M, int64_t N,
                           int64_t K, void *workspace, size_t workspace_bytes, void *stream)

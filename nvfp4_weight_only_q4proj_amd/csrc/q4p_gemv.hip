@@ -406,10 +406,24 @@ struct SkArgs {
     float g;
 };
 
-template <int ROWS, int PF, bool KR>
+// silu(gate) * up in fp32, rounded to bf16 (nearest even)
+__device__ __forceinline__ uint16_t silu_mul_bf16(float gate, float up)
+{
+    const float h = gate / (1.0f + expf(-gate)) * up;
+    return __builtin_bit_cast(uint16_t, (__bf16)h);
+}
+
+// SILU: the weight is a fused gate/up projection of 2F rows, gate rows
+// 16p..16p+15 at rows 32p.. and the matching up rows 16 rows later, so row
+// tile 2p is gate and 2p+1 up for outputs f = 16p..16p+15.  Each output pair
+// is finished as soon as both of its values are complete: in registers when
+// one wave streamed both tiles whole, otherwise through one more two-party
+// exchange word per (m, f), whose second side applies the epilogue.  out is
+// then bf16 h[M][F] instead of fp32 y[M][N].
+template <int ROWS, int PF, bool KR, bool SILU>
 __global__ void __launch_bounds__(64 * kSkMaxWaves)
 gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
-               const uint16_t *__restrict__ x, float *__restrict__ y,
+               const uint16_t *__restrict__ x, void *__restrict__ out,
                unsigned long long *__restrict__ xch, SkArgs a)
 {
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
@@ -452,6 +466,10 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     uint8_t *xl = smem;
     uint8_t *zstrip = smem + xbytes;
     floatx4_t *part = reinterpret_cast<floatx4_t *>(smem + xbytes + kZeroBytes);
+    // SILU with one K range: the first whole tile of a wave if it is an up
+    // tile and the last if it is a gate tile, when their partners are not
+    // whole in the same wave, wait here until the stream is done
+    floatx4_t *edge = part + WPG * 2 * 64;
 
     // 1. activation staging loads (rows < M, the k-tiles of this range)
     const int nthr = 64 * WPG;
@@ -555,12 +573,38 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int cfirst = n > 0 ? u0 - tfirst * KT : 0;
     int t = tfirst, c = cfirst;
 
+    float *y = static_cast<float *>(out);
+    uint16_t *hout = static_cast<uint16_t *>(out);
+    const int F = N >> 1;
+    unsigned long long *pairw = xch + kSkBoundaryWords + (int64_t)(a.KS - 1) * M * N;
+    // The complete value of output (m, col): stored, or with SILU paired with
+    // its gate/up partner
+    auto emit = [&](int m, int col, float v) {
+        const float gv = g * v;
+        if (!SILU) {
+            y[(int64_t)m * N + col] = gv;
+            return;
+        }
+        const int tt = col >> 4;
+        const int f = 16 * (tt >> 1) + (col & 15);
+        unsigned long long *wd = pairw + (int64_t)m * F + f;
+        const unsigned long long mine =
+            (1ull << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, gv);
+        const unsigned long long old =
+            __hip_atomic_exchange(wd, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (!(old >> 32))
+            return;                                     // the partner finishes the pair
+        __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        const float other = __builtin_bit_cast(float, (uint32_t)old);
+        hout[(int64_t)m * F + f] = (tt & 1) ? silu_mul_bf16(other, gv) : silu_mul_bf16(gv, other);
+    };
+
     // This range's complete value v of output (m, col) (col < N): joined with
     // the other ranges' values along the tree -- at each level the side that
     // finds its partner's value adds the two, clears the word and goes on --
     // and stored by the last join (at once when there is one range).
     auto join = [&](int m, int col, float v) {
-        for (int span = 1; span < a.KS; span *= 2) {
+        for (int span = 1; span < (KR ? a.KS : 1); span *= 2) {
             const int set = (a.KS - a.KS / span) + kr / (2 * span);
             unsigned long long *wd = xch + kSkBoundaryWords + ((int64_t)set * M + m) * N + col;
             const unsigned long long mine =
@@ -572,7 +616,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             v = __builtin_bit_cast(float, (uint32_t)old) + v;
             __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        y[(int64_t)m * N + col] = g * v;
+        emit(m, col, v);
     };
     auto store_y = [&](int tt, const floatx4_t &v) {
         const int col = 16 * tt + r;
@@ -586,6 +630,32 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                 if (m < M)
                     join(m, col, vj);
             }
+        }
+    };
+
+    // SILU with one K range: whole tiles twa..twb of this wave pair up in
+    // registers (gate tile 2p kept in gacc until up tile 2p+1 ends)
+    const int twa = cfirst == 0 ? tfirst : tfirst + 1;
+    const int twb = u1 / KT - 1;
+    floatx4_t gacc = {0.f, 0.f, 0.f, 0.f};
+    auto whole_pair = [&](int tt, const floatx4_t &v) {
+        if (tt & 1) {
+            if (tt - 1 >= twa) {
+                const int f = 8 * (tt - 1) + r;
+#pragma unroll
+                for (int j = 0; j < ROWS; ++j) {
+                    const int m = 4 * gq + j;
+                    const float gj = gacc[j], uj = v[j];
+                    if (m < M)
+                        hout[(int64_t)m * F + f] = silu_mul_bf16(g * gj, g * uj);
+                }
+            } else {
+                edge[(wave * 2) * 64 + lane] = v;
+            }
+        } else if (tt + 1 <= twb) {
+            gacc = v;
+        } else {
+            edge[(wave * 2 + 1) * 64 + lane] = v;
         }
     };
 
@@ -619,9 +689,12 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                 ++c;
                 if (c == KT || i + s == n - 1) {
                     const int cstart = (t == tfirst) ? cfirst : 0;
-                    if (cstart == 0 && c == KT)
-                        store_y(t, acc);                           // whole row tile
-                    else
+                    if (cstart == 0 && c == KT) {                  // whole row tile
+                        if (SILU && !KR)
+                            whole_pair(t, acc);
+                        else
+                            store_y(t, acc);
+                    } else
                         part[(wave * 2 + (t == tfirst ? 0 : 1)) * 64 + lane] = acc;
                     acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
                     if (c == KT) {
@@ -686,6 +759,12 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                 }
             }
         }
+    }
+    if (SILU && !KR && twa <= twb) {
+        if (twa & 1)
+            store_y(twa, edge[(wave * 2) * 64 + lane]);
+        if (!(twb & 1))
+            store_y(twb, edge[(wave * 2 + 1) * 64 + lane]);
     }
 }
 
@@ -797,31 +876,42 @@ Plan cached_plan(int64_t M, int64_t N, int64_t K)
     return p;
 }
 
-typedef void (*gemv_sk_fn)(const uint4 *, const uint2 *, const uint16_t *, float *,
+typedef void (*gemv_sk_fn)(const uint4 *, const uint2 *, const uint16_t *, void *,
                            unsigned long long *, SkArgs);
 
-template <bool KR>
+template <bool KR, bool SILU>
 gemv_sk_fn pick_sk_kernel_k(int64_t M)
 {
     switch (M) {
-    case 1: return gemv_sk_kernel<1, kSkPrefetch, KR>;
-    case 2: return gemv_sk_kernel<2, kSkPrefetch, KR>;
-    case 3: return gemv_sk_kernel<3, kSkPrefetch, KR>;
-    default: return gemv_sk_kernel<4, kSkPrefetch, KR>;
+    case 1: return gemv_sk_kernel<1, kSkPrefetch, KR, SILU>;
+    case 2: return gemv_sk_kernel<2, kSkPrefetch, KR, SILU>;
+    case 3: return gemv_sk_kernel<3, kSkPrefetch, KR, SILU>;
+    default: return gemv_sk_kernel<4, kSkPrefetch, KR, SILU>;
     }
 }
 
-gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges)
+gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges, bool silu)
 {
-    return ranges ? pick_sk_kernel_k<true>(M) : pick_sk_kernel_k<false>(M);
+    if (silu)
+        return ranges ? pick_sk_kernel_k<true, true>(M) : pick_sk_kernel_k<false, true>(M);
+    return ranges ? pick_sk_kernel_k<true, false>(M) : pick_sk_kernel_k<false, false>(M);
 }
+
+// LDS the SILU kernel with one K range adds for its deferred whole tiles
+constexpr int kSkEdgeBytes = kSkMaxWaves * 2 * 64 * 16;
+// activations of one range with those: 256-byte multiples that keep the
+// total (+ zero strip, partial sums and deferred tiles) within 160 KB
+constexpr int kSkXMaxBytesSilu = kSkXMaxBytes - 256;
+static_assert(kSkXMaxBytesSilu + kZeroBytes + 2 * kSkEdgeBytes <= 160 * 1024, "LDS budget");
 
 // K ranges for the stream-K kernel: the fewest (a power of two) whose
 // activations fit in LDS.
-int64_t sk_ranges(int64_t M, int64_t K)
+int64_t sk_ranges(int64_t M, int64_t K, bool silu)
 {
     const int64_t KT = k_tiles(K);
-    int64_t KS = 1;
+    if (M * KT * 256 <= (silu ? kSkXMaxBytesSilu : kSkXMaxBytes))
+        return 1;
+    int64_t KS = 2;
     while (KS < kSkMaxRanges && M * ((KT + KS - 1) / KS) * 256 > kSkXMaxBytes)
         KS *= 2;
     return KS;
@@ -829,9 +919,9 @@ int64_t sk_ranges(int64_t M, int64_t K)
 
 // The stream-K kernel serves a shape when its ranges' activations fit in LDS,
 // every range gets at least one k-tile, and unit indices stay below 2^31.
-bool sk_usable(int64_t M, int64_t N, int64_t K)
+bool sk_usable(int64_t M, int64_t N, int64_t K, bool silu)
 {
-    const int64_t KT = k_tiles(K), NT = n_tiles(N), KS = sk_ranges(M, K);
+    const int64_t KT = k_tiles(K), NT = n_tiles(N), KS = sk_ranges(M, K, silu);
     const int64_t KTR = (KT + KS - 1) / KS;
     return M * KTR * 256 <= kSkXMaxBytes && KT - (KS - 1) * KTR >= 1 && NT * KT < ((int64_t)1 << 31);
 }
@@ -845,10 +935,10 @@ struct SkPlan {
 // One workgroup per CU (at most kSkMaxGroups), but no more workgroups than
 // row tiles, so that every workgroup's range covers at least KT units and a
 // row tile is shared by at most two workgroups.
-SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K)
+SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
-    const int64_t KS = sk_ranges(M, K);
+    const int64_t KS = sk_ranges(M, K, silu);
     const int64_t KTR = (KT + KS - 1) / KS;
     int64_t GR = device_cus() / KS;                     // workgroups per K range
     if (GR > kSkMaxGroups / KS)
@@ -862,10 +952,12 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K)
     if (WPG > ULAST / GR)
         WPG = ULAST / GR;
     SkPlan p;
-    p.fn = pick_sk_kernel(M, KS > 1);
+    p.fn = pick_sk_kernel(M, KS > 1, silu);
     p.args = SkArgs{(int)M, (int)N, (int)K, (int)KT, (int)NT, (int)(GR * KS), (int)WPG, (int)KS,
                     (int)KTR, 0.f};
     size_t lds = (size_t)(M * KTR * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
+    if (silu && KS == 1)
+        lds += (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
     if (lds < (size_t)kSkLdsFloor)
         lds = kSkLdsFloor;
     p.lds = lds;
@@ -875,10 +967,11 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K)
 struct CachedSkPlan {
     int dev;
     int64_t M, N, K;
+    bool silu;
     SkPlan plan;
 };
 
-SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K)
+SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
 {
     static std::mutex mu;
     static std::vector<CachedSkPlan> cache;
@@ -886,12 +979,12 @@ SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K)
     (void)hipGetDevice(&dev);
     std::lock_guard<std::mutex> lock(mu);
     for (const CachedSkPlan &c : cache)
-        if (c.dev == dev && c.M == M && c.N == N && c.K == K)
+        if (c.dev == dev && c.M == M && c.N == N && c.K == K && c.silu == silu)
             return c.plan;
-    const SkPlan p = make_sk_plan(M, N, K);
+    const SkPlan p = make_sk_plan(M, N, K, silu);
     if (cache.size() >= 256)
         cache.clear();
-    cache.push_back({dev, M, N, K, p});
+    cache.push_back({dev, M, N, K, silu, p});
     return p;
 }
 
@@ -901,8 +994,21 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || M > 16 || N < 1 || K < 1)
         return 0;
-    const int64_t KS = sk_usable(M, N, K) ? sk_ranges(M, K) : 1;
+    const int64_t KS = sk_usable(M, N, K, false) ? sk_ranges(M, K, false) : 1;
     return (size_t)(kSkBoundaryWords + (KS - 1) * M * N) * sizeof(unsigned long long);
+}
+
+bool gemv_silu_mul_supported(int64_t M, int64_t F, int64_t K)
+{
+    return M >= 1 && M <= 16 && F >= 16 && F % 16 == 0 && K >= 1 && sk_usable(M, 2 * F, K, true);
+}
+
+size_t gemv_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K)
+{
+    if (!gemv_silu_mul_supported(M, F, K))
+        return 0;
+    const int64_t KS = sk_ranges(M, K, true);
+    return (size_t)(kSkBoundaryWords + (KS - 1) * M * 2 * F + M * F) * sizeof(unsigned long long);
 }
 
 hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
@@ -910,8 +1016,8 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        void *workspace, hipStream_t stream)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
-    if (sk_usable(M, N, K)) {
-        const SkPlan p = cached_sk_plan(M, N, K);
+    if (sk_usable(M, N, K, false)) {
+        const SkPlan p = cached_sk_plan(M, N, K, false);
         SkArgs args = p.args;
         args.g = g;
         hipLaunchKernelGGL(p.fn, dim3((unsigned)args.G), dim3(64 * args.WPG), p.lds, stream,
@@ -925,6 +1031,22 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        reinterpret_cast<const uint4 *>(packed_codes),
                        reinterpret_cast<const uint2 *>(packed_scales), g, x, y, (int)M, (int)N,
                        (int)K, (int)KT, (int)NT, p.TB, p.S);
+    return hipGetLastError();
+}
+
+hipError_t launch_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
+                                int64_t K, void *workspace, hipStream_t stream)
+{
+    if (!gemv_silu_mul_supported(M, F, K))
+        return hipErrorInvalidValue;
+    const SkPlan p = cached_sk_plan(M, 2 * F, K, true);
+    SkArgs args = p.args;
+    args.g = g;
+    hipLaunchKernelGGL(p.fn, dim3((unsigned)args.G), dim3(64 * args.WPG), p.lds, stream,
+                       reinterpret_cast<const uint4 *>(packed_codes),
+                       reinterpret_cast<const uint2 *>(packed_scales), x, h,
+                       static_cast<unsigned long long *>(workspace), args);
     return hipGetLastError();
 }
 

@@ -22,6 +22,16 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
                        void *workspace, hipStream_t stream);
 
+// Fused gate/up projection + silu(gate)*up (weight of 2F rows, gate and up
+// rows interleaved in blocks of 16), for the shapes the stream-K GEMV serves
+// with F % 16 == 0.
+bool gemv_silu_mul_supported(int64_t M, int64_t F, int64_t K);
+size_t gemv_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K);
+
+hipError_t launch_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
+                                int64_t K, void *workspace, hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);

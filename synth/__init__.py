@@ -190,10 +190,13 @@ WORKLOADS = {
     "pre": (3, 512, [("qkv", 3, 0, 14336, 5120), ("gate_up", 1, 0, 17408, 5120)]),
     "lmh": (4, 1, [("lm_head", 4, 0, 248320, 5120), ("up_4b", 4, 1, 9216, 2560),
                    ("down_4b", 4, 2, 2560, 9216)]),
+    # the MLP's gate and up weights as one fused [2F][K] NVFP4 weight (one
+    # global scale for both), F = 17408
+    "mlp": (5, 1, [("gate_up_fused", 1, 2, 34816, 5120)]),
 }
 
 #: workload names in listing order
-WORKLOAD_ORDER = ["tiny", "dec", "mtp", "pre", "lmh"]
+WORKLOAD_ORDER = ["tiny", "dec", "mtp", "pre", "lmh", "mlp"]
 
 _matrix_cache: dict = {}
 

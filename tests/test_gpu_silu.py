@@ -1,0 +1,154 @@
+"""q4proj_gemv_silu_mul (fused gate/up projection + silu(gate)*up, bf16 out)
+against the CPU oracle.
+
+* small and ragged shapes on every output, including shapes whose waves hold
+  many whole tiles (gate/up pairs finished in registers), single tiles
+  (pairs finished through the exchange words) and two K ranges;
+* the full decode shape (M = 1, F = 17408, K = 5120) and the verify shapes
+  M = 7 and M = 16 on sampled outputs;
+* against the unfused path: q4proj_gemv on the same packed weight gives the
+  gate and up values; silu(gate)*up of those, rounded once to bf16 in fp64,
+  is what the epilogue must return up to its own fp32 evaluation;
+* repeatability (bitwise), a workspace left zero-filled, NaN scales.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from gpu_util import DEV, note, pack, q4, to_dev_x
+
+pytestmark = pytest.mark.gpu
+
+
+def fused_matrix(seed, F, K):
+    return synth.nvfp4_normal_matrix(seed, 1, 2 * F, K)
+
+
+def run_fused(packed, g, x, F, K, workspace=None):
+    m = q4()
+    M = x.shape[0]
+    h = torch.full((M, F), -1, dtype=torch.int16, device=DEV)     # bf16 NaN pattern 0xFFFF
+    m.q4proj_gemv_silu_mul(packed[0], packed[1], g, to_dev_x(x), h, M, F, K, workspace=workspace)
+    torch.cuda.synchronize()
+    return h.cpu().numpy().view(np.uint16)
+
+
+def assert_silu_parity(mat, x, F, h, cols=None):
+    href, bound = oracle.silu_mul_cols(mat.codes, mat.scales, mat.g, x, F, cols=cols)
+    hg = h if cols is None else h[:, cols]
+    bad, worst = oracle.check_bf16(href, bound, hg)
+    assert bad == 0, f"{bad} outputs outside the allowance (worst ratio {worst:.3g})"
+    return worst
+
+
+SMALL = [(M, F, K) for M in (1, 2, 3, 5, 7, 16) for F in (16, 48, 272) for K in (16, 208, 1040)]
+
+
+@pytest.mark.parametrize("M,F,K", SMALL)
+def test_small_shapes(M, F, K):
+    mat = fused_matrix(40 + M, F, K)
+    x = synth.x_bf16(40, M, M, K)
+    note(f"gemv_silu_mul M={M} F={F} K={K}")
+    h = run_fused(pack(mat.codes, mat.scales, 2 * F, K), mat.g, x, F, K)
+    assert_silu_parity(mat, x, F, h)
+
+
+# Many row tiles per wave at short K: whole gate/up pairs finish in registers,
+# misaligned ones at the wave edges through the exchange words.
+WHOLE = [(1, 32768, 128), (3, 49152, 128), (4, 16384, 256), (16, 8192, 384), (2, 24592, 256),
+         (13, 4096, 5120)]
+
+
+@pytest.mark.parametrize("M,F,K", WHOLE)
+def test_whole_tile_pairs(M, F, K):
+    mat = fused_matrix(50, F, K)
+    x = synth.x_bf16(50, M, M, K)
+    note(f"gemv_silu_mul M={M} F={F} K={K}")
+    h = run_fused(pack(mat.codes, mat.scales, 2 * F, K), mat.g, x, F, K)
+    assert_silu_parity(mat, x, F, h)
+
+
+def sample_cols(F, n, seed):
+    rng = np.random.default_rng(seed)
+    edge = np.array([0, 1, 15, 16, 17, F // 2, F - 17, F - 16, F - 1])
+    return np.unique(np.concatenate([edge, rng.choice(F, n, replace=False)]))
+
+
+@pytest.mark.parametrize("M", [1, 7, 16])
+def test_decode_and_verify_full_size(M):
+    (c,) = synth.workload_cases("mlp")
+    mat, F, K = c.matrix, c.N // 2, c.K
+    x = c.x if M == 1 else synth.x_bf16(5, 10 + M, M, K)
+    packed = pack(mat.codes, mat.scales, 2 * F, K)
+    ws = torch.zeros(q4().q4proj_silu_mul_workspace_bytes(M, F, K), dtype=torch.uint8, device=DEV)
+    note(f"gemv_silu_mul M={M} F={F} K={K}")
+    h1 = run_fused(packed, mat.g, x, F, K, workspace=ws)
+    h2 = run_fused(packed, mat.g, x, F, K, workspace=ws)
+    assert np.array_equal(h1, h2)
+    assert int(torch.count_nonzero(ws)) == 0
+    cols = sample_cols(F, 1024 if M == 1 else 256, M)
+    worst = assert_silu_parity(mat, x, F, h1, cols)
+    print(f"fused gate/up M={M}: worst |h-h_ref|/allowance = {worst:.3g}")
+
+
+def bf16_round(v: np.ndarray) -> np.ndarray:
+    """fp64 -> bf16 bits, nearest even (via fp32: exact for these magnitudes
+    except on double-rounding ties, which the comparison below tolerates)."""
+    return torch.from_numpy(v.astype(np.float32)).to(torch.bfloat16).view(torch.int16).numpy() \
+        .view(np.uint16)
+
+
+@pytest.mark.parametrize("M,F,K", [(1, 17408, 5120), (7, 4096, 1040), (16, 2048, 5120)])
+def test_matches_unfused_gemv(M, F, K):
+    mat = fused_matrix(60, F, K)
+    x = synth.x_bf16(60, M, M, K)
+    packed = pack(mat.codes, mat.scales, 2 * F, K)
+    note(f"gemv_silu_mul vs gemv M={M} F={F} K={K}")
+    h = run_fused(packed, mat.g, x, F, K)
+    y = torch.empty((M, 2 * F), dtype=torch.float32, device=DEV)
+    q4().q4proj_gemv(packed[0], packed[1], mat.g, to_dev_x(x), y, M, 2 * F, K)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    grow, urow = oracle.gate_up_rows(F)
+    want = bf16_round(oracle.silu_mul(y[:, grow], y[:, urow]))
+    # same fp32 gate/up sums; the epilogue's fp32 silu may move a result by
+    # one bf16 step only where fp64 lies next to a rounding boundary
+    diff = np.abs(h.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1
+    assert np.mean(diff == 0) > 0.995
+
+
+def test_nan_scale_poisons_its_pair():
+    F, K, M = 64, 256, 3
+    mat = fused_matrix(70, F, K)
+    scales = mat.scales.copy()
+    scales[32 + 5, 3] = 0x7F              # gate row 16 + 5 -> output f = 21
+    scales[16 + 9, 0] = 0xFF              # up row 9 -> output f = 9
+    x = synth.x_bf16(70, M, M, K)
+    note("gemv_silu_mul NaN scales")
+    h = run_fused(pack(mat.codes, scales, 2 * F, K), mat.g, x, F, K)
+    nan = (h & 0x7FFF) > 0x7F80
+    assert nan[:, [9, 21]].all() and nan.sum() == 2 * M
+    bad, _ = oracle.check_bf16(*oracle.silu_mul_cols(mat.codes, scales, mat.g, x, F), h)
+    assert bad == 0
+
+
+def test_rejects_what_it_does_not_serve():
+    m = q4()
+    w = torch.zeros(1 << 16, dtype=torch.uint8, device=DEV)       # stands in for both packed buffers
+    ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
+    x = torch.zeros(16 * 32896, dtype=torch.int16, device=DEV)
+    h = torch.zeros(16 * 32, dtype=torch.int16, device=DEV)
+    lib = m.library()
+
+    def call(M, F, K):
+        return lib.q4proj_gemv_silu_mul(w.data_ptr(), w.data_ptr(), 1.0, x.data_ptr(), h.data_ptr(),
+                                        M, F, K, ws.data_ptr(), ws.numel(), None)
+
+    # F % 16 != 0, M > 16, K past the eight-range limit at M = 16: rejected
+    # on the host, nothing launched
+    assert call(1, 24, 128) == m.EINVAL
+    assert call(17, 16, 128) == m.EUNSUPPORTED
+    assert call(16, 16, 32896) == m.EUNSUPPORTED
