@@ -147,12 +147,11 @@ q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_sca
 
 /*
  * Device scratch q4proj_gemv_silu_mul needs for (M, F, K):
- *     8 * (65536 + (KS - 1) * M * 2F + M * F) bytes,
- * with KS the number of K ranges as for q4proj_gemv at N = 2F, except that
- * one range holds at most 130816 bytes of activations here (instead of 128
- * KiB).  The M * F words pair each gate value with its up value.  0 when the
+ *     8 * (65536 + (KS - 1) * M * F) bytes,
+ * with KS the number of K ranges as for q4proj_gemv (the joins carry a gate
+ * and an up value in one word, so each join needs M * F words).  0 when the
  * entry point does not serve the shape: M outside 1..16, F <= 0 or
- * F % 16 != 0, invalid K, or K so long that even eight ranges' activations
+ * F % 8 != 0, invalid K, or K so long that even eight ranges' activations
  * exceed 128 KiB (M * ceil(ceil(K/128) / 8) * 256 > 131072, e.g. K > 32768 at
  * M = 16).  Ownership and state as for q4proj_workspace_bytes; the two entry
  * points may share one workspace (of the larger size) on one stream.
@@ -165,22 +164,22 @@ size_t q4proj_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K);
  * "Qwen3.6 NVFP4 usage" page runs gate/up as one fused NVFP4 projection when
  * the two weights' global scales are equal, followed by a fused silu(gate)*up
  * (its environment-variable table); here the epilogue writes bf16.
- *     gate[m][f] = sum_k x[m][k] * dequant(W)[32(f/16) + f%16][k]
- *     up[m][f]   = sum_k x[m][k] * dequant(W)[32(f/16) + 16 + f%16][k]
+ *     gate[m][f] = sum_k x[m][k] * dequant(W)[16(f/8) + f%8][k]
+ *     up[m][f]   = sum_k x[m][k] * dequant(W)[16(f/8) + 8 + f%8][k]
  *     h[m][f]    = bf16( silu(gate) * up ),  silu(z) = z / (1 + exp(-z))
  * gate and up are fp32 sums as in q4proj_gemv, each scaled by the one global
  * scale g; silu and the product are evaluated in fp32 and rounded to bf16
  * (nearest even).
  * W is the fused [2F][K] weight, packed with q4proj_pack(N = 2F, K): its rows
- * alternate blocks of 16 gate rows and 16 up rows (gate rows 16p..16p+15 at
- * 32p..32p+15, up rows 16p..16p+15 at 32p+16..32p+31), so every 16-row tile
- * of the packed layout is wholly gate or wholly up.  F % 16 == 0.
+ * alternate blocks of 8 gate rows and 8 up rows (gate rows 8p..8p+7 at
+ * 16p..16p+7, up rows 8p..8p+7 at 16p+8..16p+15), so every 16-row tile of
+ * the packed layout holds both halves of its 8 outputs.  F % 8 == 0.
  *     x  uint16 [M][K] bf16 bit patterns, 16-byte aligned
  *     h  uint16 [M][F] bf16 bit patterns (output), 2-byte aligned
  * workspace: q4proj_silu_mul_workspace_bytes(M, F, K) bytes, zero-filled
  * before first use, left zero-filled by every completed call.
  * Deterministic: the same inputs give the same bits on every call.
- * Errors: EINVAL (null pointer, M/F/K <= 0, F % 16 != 0, K % 16 != 0,
+ * Errors: EINVAL (null pointer, M/F/K <= 0, F % 8 != 0, K % 16 != 0,
  *         misaligned x, h or workspace, h or workspace overlapping an input),
  *         EUNSUPPORTED (M > 16, or K too long as above), EWORKSPACE,
  *         EDEVICE, EHIP.

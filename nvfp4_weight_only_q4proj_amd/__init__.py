@@ -209,7 +209,7 @@ def q4proj_gemm(packed_codes, packed_scales, global_scale: float, x, y, M: int, 
 def q4proj_gemv_silu_mul(packed_codes, packed_scales, global_scale: float, x, h, M: int, F: int,
                          K: int, workspace=None, stream=None) -> None:
     """h[M][F] bf16 = silu(gate) * up of the fused [2F][K] gate/up weight
-    (16-row gate and up blocks alternating), 1 <= M <= 16."""
+    (8-row gate and up blocks alternating), 1 <= M <= 16."""
     dev = x.device
     N = 2 * F
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)

@@ -180,7 +180,7 @@ q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_sca
 
 size_t q4proj_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K)
 {
-    if (M <= 0 || M > Q4PROJ_GEMV_MAX_M || F <= 0 || F % 16 != 0 || F > ((int64_t)1 << 29) ||
+    if (M <= 0 || M > Q4PROJ_GEMV_MAX_M || F <= 0 || F % 8 != 0 || F > ((int64_t)1 << 29) ||
         !shape_ok(2 * F, K))
         return 0;
     return q4p::gemv_silu_mul_workspace_bytes(M, F, K);
@@ -193,7 +193,7 @@ q4proj_status q4proj_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *p
 {
     if (!packed_codes || !packed_scales || !x || !h)
         return Q4P_EINVAL;
-    if (M <= 0 || M > (int64_t)1 << 24 || F <= 0 || F % 16 != 0 || F > ((int64_t)1 << 29) ||
+    if (M <= 0 || M > (int64_t)1 << 24 || F <= 0 || F % 8 != 0 || F > ((int64_t)1 << 29) ||
         !shape_ok(2 * F, K))
         return Q4P_EINVAL;
     if (!aligned(packed_codes, 16) || !aligned(packed_scales, 8) || !aligned(x, 16) ||

@@ -413,13 +413,47 @@ __device__ __forceinline__ uint16_t silu_mul_bf16(float gate, float up)
     return __builtin_bit_cast(uint16_t, (__bf16)h);
 }
 
-// SILU: the weight is a fused gate/up projection of 2F rows, gate rows
-// 16p..16p+15 at rows 32p.. and the matching up rows 16 rows later, so row
-// tile 2p is gate and 2p+1 up for outputs f = 16p..16p+15.  Each output pair
-// is finished as soon as both of its values are complete: in registers when
-// one wave streamed both tiles whole, otherwise through one more two-party
-// exchange word per (m, f), whose second side applies the epilogue.  out is
-// then bf16 h[M][F] instead of fp32 y[M][N].
+// lane r <- lane r ^ 8 within each 16-lane row (a row rotate by 8)
+__device__ __forceinline__ float swap8(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
+// A gate/up pair of partial sums in one 64-bit exchange word.  Both fields
+// are XORed with a NaN pattern that no stored value has (a NaN is stored as
+// the one canonical quiet NaN), so a word holding a pair is never zero and
+// zero still means empty.
+constexpr uint32_t kPairKey = 0x7FC00001u;
+
+__device__ __forceinline__ uint32_t pair_field(float v)
+{
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    return ((b & 0x7FFFFFFFu) > 0x7F800000u ? 0x7FC00000u : b) ^ kPairKey;
+}
+
+__device__ __forceinline__ unsigned long long pair_word(float gate, float up)
+{
+    return ((unsigned long long)pair_field(up) << 32) | pair_field(gate);
+}
+
+__device__ __forceinline__ float pair_gate(unsigned long long w)
+{
+    return __builtin_bit_cast(float, (uint32_t)w ^ kPairKey);
+}
+
+__device__ __forceinline__ float pair_up(unsigned long long w)
+{
+    return __builtin_bit_cast(float, (uint32_t)(w >> 32) ^ kPairKey);
+}
+
+// SILU: the weight is a fused gate/up projection of 2F rows in which 8 gate
+// rows and the matching 8 up rows alternate, so row tile t holds the gate
+// rows (lanes r < 8) and the up rows (lanes r >= 8) of outputs f = 8t..8t+7.
+// Wherever a tile's values complete, a row rotate hands lane r + 8's value
+// to lane r; exchanges between workgroups and K ranges then carry (gate, up)
+// in one word from lane r, and the side that completes a pair applies the
+// epilogue.  out is bf16 h[M][F] instead of fp32 y[M][N].
 template <int ROWS, int PF, bool KR, bool SILU>
 __global__ void __launch_bounds__(64 * kSkMaxWaves)
 gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
@@ -466,10 +500,6 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     uint8_t *xl = smem;
     uint8_t *zstrip = smem + xbytes;
     floatx4_t *part = reinterpret_cast<floatx4_t *>(smem + xbytes + kZeroBytes);
-    // SILU with one K range: the first whole tile of a wave if it is an up
-    // tile and the last if it is a gate tile, when their partners are not
-    // whole in the same wave, wait here until the stream is done
-    floatx4_t *edge = part + WPG * 2 * 64;
 
     // 1. activation staging loads (rows < M, the k-tiles of this range)
     const int nthr = 64 * WPG;
@@ -576,28 +606,6 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     float *y = static_cast<float *>(out);
     uint16_t *hout = static_cast<uint16_t *>(out);
     const int F = N >> 1;
-    unsigned long long *pairw = xch + kSkBoundaryWords + (int64_t)(a.KS - 1) * M * N;
-    // The complete value of output (m, col): stored, or with SILU paired with
-    // its gate/up partner
-    auto emit = [&](int m, int col, float v) {
-        const float gv = g * v;
-        if (!SILU) {
-            y[(int64_t)m * N + col] = gv;
-            return;
-        }
-        const int tt = col >> 4;
-        const int f = 16 * (tt >> 1) + (col & 15);
-        unsigned long long *wd = pairw + (int64_t)m * F + f;
-        const unsigned long long mine =
-            (1ull << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, gv);
-        const unsigned long long old =
-            __hip_atomic_exchange(wd, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        if (!(old >> 32))
-            return;                                     // the partner finishes the pair
-        __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        const float other = __builtin_bit_cast(float, (uint32_t)old);
-        hout[(int64_t)m * F + f] = (tt & 1) ? silu_mul_bf16(other, gv) : silu_mul_bf16(gv, other);
-    };
 
     // This range's complete value v of output (m, col) (col < N): joined with
     // the other ranges' values along the tree -- at each level the side that
@@ -616,46 +624,51 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             v = __builtin_bit_cast(float, (uint32_t)old) + v;
             __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        emit(m, col, v);
+        y[(int64_t)m * N + col] = g * v;
     };
+    // SILU: the same for this range's complete gate and up values of output
+    // (m, f), one word per pair; the last join applies the epilogue
+    auto join_pair = [&](int m, int f, float vg, float vu) {
+        for (int span = 1; span < (KR ? a.KS : 1); span *= 2) {
+            const int set = (a.KS - a.KS / span) + kr / (2 * span);
+            unsigned long long *wd = xch + kSkBoundaryWords + ((int64_t)set * M + m) * F + f;
+            const unsigned long long old = __hip_atomic_exchange(
+                wd, pair_word(vg, vu), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old == 0ull)
+                return;
+            vg = pair_gate(old) + vg;
+            vu = pair_up(old) + vu;
+            __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        hout[(int64_t)m * F + f] = silu_mul_bf16(g * vg, g * vu);
+    };
+    // Row tile tt complete in this range: lane (r, gq) holds rows 4gq + j of
+    // output column 16tt + r.  Called with the whole wave active (the row
+    // rotate reads every lane).
     auto store_y = [&](int tt, const floatx4_t &v) {
-        const int col = 16 * tt + r;
-        if (col < N) {
+        if (SILU) {
+            const int f = 8 * tt + r;
 #pragma unroll
             for (int j = 0; j < ROWS; ++j) {
                 const int m = 4 * gq + j;
                 // copy the element out first: clang mis-lowers a bit_cast whose
                 // operand is a vector element (it reads element 0)
+                const float vg = v[j];
+                const float vu = swap8(vg);
+                if (r < 8 && m < M)
+                    join_pair(m, f, vg, vu);
+            }
+            return;
+        }
+        const int col = 16 * tt + r;
+        if (col < N) {
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j) {
+                const int m = 4 * gq + j;
                 const float vj = v[j];
                 if (m < M)
                     join(m, col, vj);
             }
-        }
-    };
-
-    // SILU with one K range: whole tiles twa..twb of this wave pair up in
-    // registers (gate tile 2p kept in gacc until up tile 2p+1 ends)
-    const int twa = cfirst == 0 ? tfirst : tfirst + 1;
-    const int twb = u1 / KT - 1;
-    floatx4_t gacc = {0.f, 0.f, 0.f, 0.f};
-    auto whole_pair = [&](int tt, const floatx4_t &v) {
-        if (tt & 1) {
-            if (tt - 1 >= twa) {
-                const int f = 8 * (tt - 1) + r;
-#pragma unroll
-                for (int j = 0; j < ROWS; ++j) {
-                    const int m = 4 * gq + j;
-                    const float gj = gacc[j], uj = v[j];
-                    if (m < M)
-                        hout[(int64_t)m * F + f] = silu_mul_bf16(g * gj, g * uj);
-                }
-            } else {
-                edge[(wave * 2) * 64 + lane] = v;
-            }
-        } else if (tt + 1 <= twb) {
-            gacc = v;
-        } else {
-            edge[(wave * 2 + 1) * 64 + lane] = v;
         }
     };
 
@@ -689,12 +702,9 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                 ++c;
                 if (c == KT || i + s == n - 1) {
                     const int cstart = (t == tfirst) ? cfirst : 0;
-                    if (cstart == 0 && c == KT) {                  // whole row tile
-                        if (SILU && !KR)
-                            whole_pair(t, acc);
-                        else
-                            store_y(t, acc);
-                    } else
+                    if (cstart == 0 && c == KT)
+                        store_y(t, acc);                           // whole row tile
+                    else
                         part[(wave * 2 + (t == tfirst ? 0 : 1)) * 64 + lane] = acc;
                     acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
                     if (c == KT) {
@@ -739,6 +749,24 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
         // boundary between groups bnd, bnd + 1 of this range
         const int bnd = kr * GR + (ta < UW0 ? L - 1 : L);
         unsigned long long *slot = xch + ((int64_t)bnd * 64 + lane) * 4;
+        if (SILU) {
+#pragma unroll
+            for (int j = 0; j < ROWS; ++j) {
+                const int m = 4 * gq + j;
+                const float sg = sum[j];
+                const float su = swap8(sg);
+                if (r < 8 && m < M) {
+                    const unsigned long long old = __hip_atomic_exchange(
+                        slot + j, pair_word(sg, su), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (old != 0ull) {
+                        __hip_atomic_store(slot + j, 0ull, __ATOMIC_RELAXED,
+                                           __HIP_MEMORY_SCOPE_AGENT);
+                        join_pair(m, 8 * tau + r, pair_gate(old) + sg, pair_up(old) + su);
+                    }
+                }
+            }
+            continue;
+        }
         const int col = 16 * tau + r;
 #pragma unroll
         for (int j = 0; j < ROWS; ++j) {
@@ -759,12 +787,6 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                 }
             }
         }
-    }
-    if (SILU && !KR && twa <= twb) {
-        if (twa & 1)
-            store_y(twa, edge[(wave * 2) * 64 + lane]);
-        if (!(twb & 1))
-            store_y(twb, edge[(wave * 2 + 1) * 64 + lane]);
     }
 }
 
@@ -897,21 +919,12 @@ gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges, bool silu)
     return ranges ? pick_sk_kernel_k<true, false>(M) : pick_sk_kernel_k<false, false>(M);
 }
 
-// LDS the SILU kernel with one K range adds for its deferred whole tiles
-constexpr int kSkEdgeBytes = kSkMaxWaves * 2 * 64 * 16;
-// activations of one range with those: 256-byte multiples that keep the
-// total (+ zero strip, partial sums and deferred tiles) within 160 KB
-constexpr int kSkXMaxBytesSilu = kSkXMaxBytes - 256;
-static_assert(kSkXMaxBytesSilu + kZeroBytes + 2 * kSkEdgeBytes <= 160 * 1024, "LDS budget");
-
 // K ranges for the stream-K kernel: the fewest (a power of two) whose
 // activations fit in LDS.
-int64_t sk_ranges(int64_t M, int64_t K, bool silu)
+int64_t sk_ranges(int64_t M, int64_t K)
 {
     const int64_t KT = k_tiles(K);
-    if (M * KT * 256 <= (silu ? kSkXMaxBytesSilu : kSkXMaxBytes))
-        return 1;
-    int64_t KS = 2;
+    int64_t KS = 1;
     while (KS < kSkMaxRanges && M * ((KT + KS - 1) / KS) * 256 > kSkXMaxBytes)
         KS *= 2;
     return KS;
@@ -919,9 +932,9 @@ int64_t sk_ranges(int64_t M, int64_t K, bool silu)
 
 // The stream-K kernel serves a shape when its ranges' activations fit in LDS,
 // every range gets at least one k-tile, and unit indices stay below 2^31.
-bool sk_usable(int64_t M, int64_t N, int64_t K, bool silu)
+bool sk_usable(int64_t M, int64_t N, int64_t K)
 {
-    const int64_t KT = k_tiles(K), NT = n_tiles(N), KS = sk_ranges(M, K, silu);
+    const int64_t KT = k_tiles(K), NT = n_tiles(N), KS = sk_ranges(M, K);
     const int64_t KTR = (KT + KS - 1) / KS;
     return M * KTR * 256 <= kSkXMaxBytes && KT - (KS - 1) * KTR >= 1 && NT * KT < ((int64_t)1 << 31);
 }
@@ -938,7 +951,7 @@ struct SkPlan {
 SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
-    const int64_t KS = sk_ranges(M, K, silu);
+    const int64_t KS = sk_ranges(M, K);
     const int64_t KTR = (KT + KS - 1) / KS;
     int64_t GR = device_cus() / KS;                     // workgroups per K range
     if (GR > kSkMaxGroups / KS)
@@ -956,8 +969,6 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
     p.args = SkArgs{(int)M, (int)N, (int)K, (int)KT, (int)NT, (int)(GR * KS), (int)WPG, (int)KS,
                     (int)KTR, 0.f};
     size_t lds = (size_t)(M * KTR * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
-    if (silu && KS == 1)
-        lds += (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
     if (lds < (size_t)kSkLdsFloor)
         lds = kSkLdsFloor;
     p.lds = lds;
@@ -994,21 +1005,21 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || M > 16 || N < 1 || K < 1)
         return 0;
-    const int64_t KS = sk_usable(M, N, K, false) ? sk_ranges(M, K, false) : 1;
+    const int64_t KS = sk_usable(M, N, K) ? sk_ranges(M, K) : 1;
     return (size_t)(kSkBoundaryWords + (KS - 1) * M * N) * sizeof(unsigned long long);
 }
 
 bool gemv_silu_mul_supported(int64_t M, int64_t F, int64_t K)
 {
-    return M >= 1 && M <= 16 && F >= 16 && F % 16 == 0 && K >= 1 && sk_usable(M, 2 * F, K, true);
+    return M >= 1 && M <= 16 && F >= 8 && F % 8 == 0 && K >= 1 && sk_usable(M, 2 * F, K);
 }
 
 size_t gemv_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K)
 {
     if (!gemv_silu_mul_supported(M, F, K))
         return 0;
-    const int64_t KS = sk_ranges(M, K, true);
-    return (size_t)(kSkBoundaryWords + (KS - 1) * M * 2 * F + M * F) * sizeof(unsigned long long);
+    const int64_t KS = sk_ranges(M, K);
+    return (size_t)(kSkBoundaryWords + (KS - 1) * M * F) * sizeof(unsigned long long);
 }
 
 hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
@@ -1016,7 +1027,7 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        void *workspace, hipStream_t stream)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
-    if (sk_usable(M, N, K, false)) {
+    if (sk_usable(M, N, K)) {
         const SkPlan p = cached_sk_plan(M, N, K, false);
         SkArgs args = p.args;
         args.g = g;

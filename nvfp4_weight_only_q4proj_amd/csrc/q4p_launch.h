@@ -23,8 +23,8 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        void *workspace, hipStream_t stream);
 
 // Fused gate/up projection + silu(gate)*up (weight of 2F rows, gate and up
-// rows interleaved in blocks of 16), for the shapes the stream-K GEMV serves
-// with F % 16 == 0.
+// rows alternating in blocks of 8), for the shapes the stream-K GEMV serves,
+// F % 8 == 0.
 bool gemv_silu_mul_supported(int64_t M, int64_t F, int64_t K);
 size_t gemv_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K);
 

@@ -13,7 +13,7 @@ with gcc into ``liboracle.so`` and exposes numpy-level wrappers:
 * :func:`check` — the acceptance test |y_gpu - y_ref| <= rtol * S,
 * :func:`silu_mul_cols` / :func:`check_bf16` — the fused gate/up projection
   h = silu(gate) * up on a weight whose gate and up rows are interleaved in
-  groups of 16, its error allowance, and the bf16 acceptance test.
+  groups of 8, its error allowance, and the bf16 acceptance test.
 
 Formats and layouts are documented at the top of ``oracle.c``.
 """
@@ -164,10 +164,10 @@ def check(y_ref, S, y_gpu, rtol: float = RTOL, lib=None):
 
 def gate_up_rows(F: int):
     """Rows of the fused [2F][K] weight holding gate row f and up row f
-    (interleaved in groups of 16: gate rows 16p.. at 32p.., up rows 16 later)."""
+    (interleaved in groups of 8: gate rows 8p.. at 16p.., up rows 8 later)."""
     f = np.arange(F, dtype=np.int64)
-    gate = 32 * (f // 16) + f % 16
-    return gate, gate + 16
+    gate = 16 * (f // 8) + f % 8
+    return gate, gate + 8
 
 
 def silu_mul(gate, up, lib=None) -> np.ndarray:

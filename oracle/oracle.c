@@ -258,9 +258,9 @@ int64_t orc_check(int64_t count, const double *yref, const double *S,
  * silu(z) = z * sigmoid(z) = z / (1 + exp(-z)) (the SwiGLU gate).
  *
  * This library's fused weight (a reading; the page gives no layout) stacks
- * gate and up rows interleaved in groups of 16: rows 32p..32p+15 are gate rows
- * 16p..16p+15 and rows 32p+16..32p+31 are up rows 16p..16p+15, so gate row f
- * sits at 32*(f/16) + f%16 and up row f 16 rows later.  The row selection is
+ * gate and up rows interleaved in groups of 8: rows 16p..16p+7 are gate rows
+ * 8p..8p+7 and rows 16p+8..16p+15 are up rows 8p..8p+7, so gate row f sits
+ * at 16*(f/8) + f%8 and up row f 8 rows later.  The row selection is
  * done by the Python wrapper; this file supplies the fp64 arithmetic.
  */
 void orc_silu_mul(int64_t count, const double *gate, const double *up, double *h)

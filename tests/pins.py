@@ -322,11 +322,11 @@ def pin_silu_mul_torch(lib):
     assert abs(h0[2] + 1.0 / (1.0 + math.e)) < 1e-15
 
 
-def _interleave16(gate, up):
-    """Stack [F][W] gate and up row blocks as the fused weight: groups of 16
-    gate rows then 16 up rows (F a multiple of 16)."""
+def _interleave8(gate, up):
+    """Stack [F][W] gate and up row blocks as the fused weight: groups of 8
+    gate rows then 8 up rows (F a multiple of 8)."""
     F, W = gate.shape
-    return np.stack([gate.reshape(F // 16, 16, W), up.reshape(F // 16, 16, W)], axis=1).reshape(2 * F, W)
+    return np.stack([gate.reshape(F // 8, 8, W), up.reshape(F // 8, 8, W)], axis=1).reshape(2 * F, W)
 
 
 def pin_silu_mul_fused_rows(lib):
@@ -337,15 +337,15 @@ def pin_silu_mul_fused_rows(lib):
     mg = synth.nvfp4_normal_matrix(81, 1, F, K, threads=1)
     mu = synth.nvfp4_normal_matrix(81, 2, F, K, threads=1)
     x = synth.x_bf16(81, 3, M, K, threads=1)
-    codes = _interleave16(mg.codes, mu.codes)
-    scales = _interleave16(mg.scales, mu.scales)
+    codes = _interleave8(mg.codes, mu.codes)
+    scales = _interleave8(mg.scales, mu.scales)
     g = 0.75                                       # one global scale for both halves
     h, _ = oracle.silu_mul_cols(codes, scales, g, x, F, lib=lib)
     a, _ = oracle.proj(mg.codes, mg.scales, g, x, lib=lib)
     b, _ = oracle.proj(mu.codes, mu.scales, g, x, lib=lib)
     ref = (torch.nn.functional.silu(torch.from_numpy(a)) * torch.from_numpy(b)).numpy()
     assert np.allclose(h, ref, rtol=1e-13, atol=1e-300)
-    cols = np.array([0, 15, 16, 47])
+    cols = np.array([0, 7, 8, 15, 16, 47])
     hc, _ = oracle.silu_mul_cols(codes, scales, g, x, F, cols=cols, lib=lib)
     assert np.array_equal(hc, h[:, cols])
 

@@ -66,13 +66,11 @@ def test_workspace_of_the_verify_shape(q4):
 
 
 def silu_ranges(M, K):
-    """K ranges of the fused gate/up GEMV: one while M x k-tiles x 256 B of
-    activations stay within 130816 B, else the fewest of 2, 4, 8 whose
-    ranges stay within 128 KiB (None: not served)."""
+    """K ranges of the fused gate/up GEMV, as for the plain GEMV: the fewest
+    of 1, 2, 4, 8 whose activations (M x k-tiles x 256 B) stay within 128 KiB
+    (None: not served)."""
     kt = -(-K // 128)
-    if M * kt * 256 <= 130816:
-        return 1
-    ks = 2
+    ks = 1
     while ks < 8 and M * -(-kt // ks) * 256 > 128 * 1024:
         ks *= 2
     return ks if M * -(-kt // ks) * 256 <= 128 * 1024 else None
@@ -83,17 +81,18 @@ def silu_ranges(M, K):
                                  (64, 32768), (64, 65536), (64, 262144)])
 def test_silu_mul_workspace(q4, M, F, K):
     ks = silu_ranges(M, K)
-    want = 0 if ks is None else 8 * (65536 + (ks - 1) * M * 2 * F + M * F)
+    want = 0 if ks is None else 8 * (65536 + (ks - 1) * M * F)
     assert q4.q4proj_silu_mul_workspace_bytes(M, F, K) == want
 
 
 def test_silu_mul_workspace_limits(q4):
-    # one range up to 130816 B of activations (M x k-tiles = 511), two above
-    assert q4.q4proj_silu_mul_workspace_bytes(7, 64, 73 * 128) == 8 * (65536 + 7 * 64)
-    assert q4.q4proj_silu_mul_workspace_bytes(8, 64, 64 * 128) == 8 * (65536 + 8 * 128 + 8 * 64)
+    # one range up to 128 KiB of activations (M x k-tiles = 512), two above
+    assert q4.q4proj_silu_mul_workspace_bytes(8, 64, 64 * 128) == 8 * 65536
+    assert q4.q4proj_silu_mul_workspace_bytes(8, 64, 65 * 128) == 8 * (65536 + 8 * 64)
+    assert q4.q4proj_silu_mul_workspace_bytes(1, 8, 128) == 8 * 65536
     assert q4.q4proj_silu_mul_workspace_bytes(16, 64, 32768) > 0
     assert q4.q4proj_silu_mul_workspace_bytes(16, 64, 32768 + 128) == 0
-    for M, F, K in [(0, 16, 128), (17, 16, 128), (1, 8, 128), (1, 24, 128), (1, 0, 128),
+    for M, F, K in [(0, 16, 128), (17, 16, 128), (1, 4, 128), (1, 12, 128), (1, 0, 128),
                     (1, 16, 120), (1, 16, 0)]:
         assert q4.q4proj_silu_mul_workspace_bytes(M, F, K) == 0, (M, F, K)
 
@@ -149,21 +148,21 @@ def test_gemv_m_range(q4):
     assert proj(lib, "q4proj_gemv", M=1000) == q4.EUNSUPPORTED
 
 
-def silu(lib, pc=A, ps=B, x=X, h=Y, M=1, F=64, K=256, ws=W, wsb=WSB + 8 * 64):
+def silu(lib, pc=A, ps=B, x=X, h=Y, M=1, F=64, K=256, ws=W, wsb=WSB):
     return lib.q4proj_gemv_silu_mul(pc, ps, ctypes.c_float(1.0), x, h, M, F, K, ws, wsb, None)
 
 
 def test_silu_mul_validation(q4):
     lib = q4.library()
-    assert q4.q4proj_silu_mul_workspace_bytes(1, 64, 256) == WSB + 8 * 64
+    assert q4.q4proj_silu_mul_workspace_bytes(1, 64, 256) == WSB
     for kw in [dict(pc=None), dict(ps=None), dict(x=None), dict(h=None), dict(M=0), dict(F=0),
-               dict(F=24), dict(F=-16), dict(K=0), dict(K=24), dict(x=X + 8), dict(pc=A + 4),
+               dict(F=12), dict(F=-16), dict(K=0), dict(K=24), dict(x=X + 8), dict(pc=A + 4),
                dict(ps=B + 4), dict(h=Y + 1), dict(h=X + 64), dict(h=A), dict(ws=None),
                dict(ws=W + 4), dict(ws=Y - 4096), dict(ws=X)]:
         assert silu(lib, **kw) == q4.EINVAL, kw
     assert silu(lib, M=17) == q4.EUNSUPPORTED
     assert silu(lib, M=16, K=32768 + 128) == q4.EUNSUPPORTED
-    assert silu(lib, wsb=WSB + 8 * 64 - 8) == q4.EWORKSPACE
+    assert silu(lib, wsb=WSB - 8) == q4.EWORKSPACE
     assert silu(lib, ws=None, wsb=0) == q4.EWORKSPACE
 
 
