@@ -20,10 +20,11 @@ Also measured and reported in the same JSON line:
                 `traffic` (HBM bytes per launch, mean of the two) from the
                 rocprofv3 counter summary in profiles/ when current.
   shapes        the other workloads' GEMVs (M = 7 verify, lm-head, 4B shapes).
-  fused_gate_up the MLP's gate and up weights as one fused 2F x K NVFP4 GEMV
-                with the silu(gate)*up epilogue (bf16 out), F = 17408, K = 5120,
-                at M = 1 and M = 7, beside the plain GEMV over the same packed
-                weight (fp32 out, no epilogue).
+  fused_gate_up the MLP's gate and up weights as one fused 2F x K NVFP4
+                projection with the silu(gate)*up epilogue (bf16 out), F = 17408,
+                K = 5120: the GEMV at M = 1 and M = 7 and the GEMM at M = 512,
+                each beside the plain projection over the same packed weight
+                (fp32 out, no epilogue).
   pack          the one-time weight swizzle (read + write bytes / s).
   cpu_baseline  the CPU oracle on the decode step, on the host cores.
 """
@@ -302,10 +303,37 @@ def main():
                 "hbm_frac": round(b_fused / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                 "plain_gemv_2F_us": round(ms_p * 1e3, 2)}
             del u, h, ws
+        # the M = 512 prefill chunk through the matrix-core path
+        (cp,) = synth.workload_cases("pre", only=["gate_up"])
+        M = cp.M
+        cm = synth.Case("mlp", c.name, M, c.matrix, cp.x)
+        u = upload(cm, copies_for(algo_bytes(M, 2 * F, K)))
+        h = torch.empty((M, F), dtype=torch.int16, device=dev)
+
+        def fused_gemm(i, u=u, h=h):
+            pc, ps = u["w"][i % len(u["w"])]
+            return lambda: q4.q4proj_gemm_silu_mul(pc, ps, u["g"], u["x"], h, M, F, K)
+
+        n = max(10, args.steps // 8)
+        for i in range(3):
+            fused_gemm(i)()
+            launcher("gemm", u, i)()
+        ms_f, _ = timed_region(torch, [fused_gemm(i) for i in range(n)], n)
+        ms_p, _ = timed_region(torch, [launcher("gemm", u, i) for i in range(n)], n)
+        flop = 2.0 * M * 2 * F * K
+        fused[f"M={M}"] = {
+            "M": M, "F": F, "K": K, "us": round(ms_f * 1e3, 2),
+            "tflops": round(flop / (ms_f * 1e-3) / 1e12, 1),
+            "mfma_frac": round(flop / (ms_f * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "plain_gemm_2F_us": round(ms_p * 1e3, 2)}
+        del u, h
         out["fused_gate_up"] = {
-            "workload": "fused gate/up 5120 -> 2x17408 NVFP4 GEMV + silu(gate)*up -> bf16",
-            "kernel": "gemv_sk_kernel<ROWS, 4, false, true>", "per_M": fused,
-            "kernel_source_sha256_16": src_digest("q4p_gemv.hip")}
+            "workload": "fused gate/up 5120 -> 2x17408 NVFP4 projection + silu(gate)*up -> bf16",
+            "kernels": ["gemv_sk_kernel<ROWS, 4, false, true> (M <= 16)",
+                        "gemm_kernel<4, 1, true> (M = 512)"],
+            "per_M": fused,
+            "kernel_source_sha256_16": {"gemv": src_digest("q4p_gemv.hip"),
+                                        "gemm": src_digest("q4p_gemm.hip")}}
 
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

@@ -189,6 +189,21 @@ q4proj_status q4proj_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                    int64_t M, int64_t F, int64_t K, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/*
+ * q4proj_gemm_silu_mul — the same fused gate/up projection and epilogue as
+ * q4proj_gemv_silu_mul for any M >= 1 (sized for the M = 512 prefill chunk):
+ * the bf16 matrix-core projection of q4proj_gemm over the fused [2F][K]
+ * weight, h[M][F] = bf16(silu(g*gate) * (g*up)) written in place of y.
+ * Same layouts and result definition as q4proj_gemv_silu_mul; workspace is
+ * not used (may be NULL with workspace_bytes 0).  Deterministic.
+ * Errors: EINVAL (null pointer, M/F/K <= 0, F % 8 != 0, K % 16 != 0,
+ *         misaligned x or h, h overlapping an input), EDEVICE, EHIP.
+ */
+q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                   float global_scale, const uint16_t *x, uint16_t *h,
+                                   int64_t M, int64_t F, int64_t K, void *workspace,
+                                   size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *q4proj_status_string(q4proj_status s);
 

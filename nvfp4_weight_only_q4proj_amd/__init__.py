@@ -50,6 +50,8 @@ _lib.q4proj_silu_mul_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.q4proj_silu_mul_workspace_bytes.restype = _sz
 _lib.q4proj_gemv_silu_mul.argtypes = _PROJ_ARGS
 _lib.q4proj_gemv_silu_mul.restype = ctypes.c_int
+_lib.q4proj_gemm_silu_mul.argtypes = _PROJ_ARGS
+_lib.q4proj_gemm_silu_mul.restype = ctypes.c_int
 _lib.q4proj_status_string.argtypes = [ctypes.c_int]
 _lib.q4proj_status_string.restype = ctypes.c_char_p
 _lib.q4proj_last_hip_error.argtypes = []
@@ -58,7 +60,7 @@ _lib.q4proj_last_hip_error.restype = ctypes.c_char_p
 #: Exported symbols declared by include/q4proj.h.
 SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
            "q4proj_pack", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
-           "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul",
+           "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul", "q4proj_gemm_silu_mul",
            "q4proj_status_string", "q4proj_last_hip_error")
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE, EWORKSPACE, EHIP = range(6)
@@ -210,6 +212,19 @@ def q4proj_gemv_silu_mul(packed_codes, packed_scales, global_scale: float, x, h,
                          K: int, workspace=None, stream=None) -> None:
     """h[M][F] bf16 = silu(gate) * up of the fused [2F][K] gate/up weight
     (8-row gate and up blocks alternating), 1 <= M <= 16."""
+    _silu_mul(_lib.q4proj_gemv_silu_mul, "q4proj_gemv_silu_mul", packed_codes, packed_scales,
+              global_scale, x, h, M, F, K, workspace, stream)
+
+
+def q4proj_gemm_silu_mul(packed_codes, packed_scales, global_scale: float, x, h, M: int, F: int,
+                         K: int, workspace=None, stream=None) -> None:
+    """As q4proj_gemv_silu_mul for any M >= 1 (matrix-core path, no workspace)."""
+    _silu_mul(_lib.q4proj_gemm_silu_mul, "q4proj_gemm_silu_mul", packed_codes, packed_scales,
+              global_scale, x, h, M, F, K, workspace, stream)
+
+
+def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, K, workspace,
+              stream):
     dev = x.device
     N = 2 * F
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
@@ -219,16 +234,15 @@ def q4proj_gemv_silu_mul(packed_codes, packed_scales, global_scale: float, x, h,
     _need(x, "x", x.dtype, M * K, dev)
     _need(h, "h", h.dtype, M * F, dev)
     ws_ptr, ws_bytes = None, 0
-    if workspace is None:
+    if workspace is None and fn is _lib.q4proj_gemv_silu_mul:
         workspace = default_workspace(dev, q4proj_silu_mul_workspace_bytes(M, F, K))
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
     with torch.cuda.device(dev):
-        _check(_lib.q4proj_gemv_silu_mul(packed_codes.data_ptr(), packed_scales.data_ptr(),
-                                         float(global_scale), x.data_ptr(), h.data_ptr(), M, F, K,
-                                         ws_ptr, ws_bytes, _stream(x, stream)),
-               "q4proj_gemv_silu_mul")
+        _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
+                  x.data_ptr(), h.data_ptr(), M, F, K, ws_ptr, ws_bytes, _stream(x, stream)),
+               where)
 
 
 def pack_weight(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, stream=None):

@@ -88,6 +88,26 @@ q4proj_status check_projection(const uint8_t *pc, const uint8_t *ps, const uint1
     return Q4P_OK;
 }
 
+// Arguments of the fused gate/up entry points (h: bf16 [M][F]).
+q4proj_status check_silu_mul(const uint8_t *pc, const uint8_t *ps, const uint16_t *x,
+                             const uint16_t *h, int64_t M, int64_t F, int64_t K)
+{
+    if (!pc || !ps || !x || !h)
+        return Q4P_EINVAL;
+    if (M <= 0 || M > (int64_t)1 << 24 || F <= 0 || F % 8 != 0 || F > ((int64_t)1 << 29) ||
+        !shape_ok(2 * F, K))
+        return Q4P_EINVAL;
+    if ((uint64_t)M * (uint64_t)F > ((uint64_t)1 << 40))
+        return Q4P_EINVAL;
+    if (!aligned(pc, 16) || !aligned(ps, 8) || !aligned(x, 16) || !aligned(h, 2))
+        return Q4P_EINVAL;
+    const size_t hbytes = (size_t)M * (size_t)F * 2, xbytes = (size_t)M * (size_t)K * 2;
+    if (overlap(h, hbytes, x, xbytes) || overlap(h, hbytes, pc, q4proj_packed_codes_bytes(2 * F, K)) ||
+        overlap(h, hbytes, ps, q4proj_packed_scales_bytes(2 * F, K)))
+        return Q4P_EINVAL;
+    return Q4P_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -191,20 +211,12 @@ q4proj_status q4proj_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                    int64_t F, int64_t K, void *workspace, size_t workspace_bytes,
                                    void *stream)
 {
-    if (!packed_codes || !packed_scales || !x || !h)
-        return Q4P_EINVAL;
-    if (M <= 0 || M > (int64_t)1 << 24 || F <= 0 || F % 8 != 0 || F > ((int64_t)1 << 29) ||
-        !shape_ok(2 * F, K))
-        return Q4P_EINVAL;
-    if (!aligned(packed_codes, 16) || !aligned(packed_scales, 8) || !aligned(x, 16) ||
-        !aligned(h, 2))
-        return Q4P_EINVAL;
+    q4proj_status st = check_silu_mul(packed_codes, packed_scales, x, h, M, F, K);
+    if (st != Q4P_OK)
+        return st;
     const int64_t N = 2 * F;
     const size_t hbytes = (size_t)M * (size_t)F * 2, xbytes = (size_t)M * (size_t)K * 2;
     const size_t pcb = q4proj_packed_codes_bytes(N, K), psb = q4proj_packed_scales_bytes(N, K);
-    if (overlap(h, hbytes, x, xbytes) || overlap(h, hbytes, packed_codes, pcb) ||
-        overlap(h, hbytes, packed_scales, psb))
-        return Q4P_EINVAL;
     if (M > Q4PROJ_GEMV_MAX_M)
         return Q4P_EUNSUPPORTED;
     const size_t need = q4proj_silu_mul_workspace_bytes(M, F, K);
@@ -217,12 +229,29 @@ q4proj_status q4proj_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *p
     if (overlap(workspace, need, h, hbytes) || overlap(workspace, need, x, xbytes) ||
         overlap(workspace, need, packed_codes, pcb) || overlap(workspace, need, packed_scales, psb))
         return Q4P_EINVAL;
-    q4proj_status st = check_device();
+    st = check_device();
     if (st != Q4P_OK)
         return st;
     return record_hip(q4p::launch_gemv_silu_mul(packed_codes, packed_scales, global_scale, x, h,
                                                 M, F, K, workspace,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                   float global_scale, const uint16_t *x, uint16_t *h, int64_t M,
+                                   int64_t F, int64_t K, void *workspace, size_t workspace_bytes,
+                                   void *stream)
+{
+    (void)workspace;
+    (void)workspace_bytes;
+    q4proj_status st = check_silu_mul(packed_codes, packed_scales, x, h, M, F, K);
+    if (st != Q4P_OK)
+        return st;
+    st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_gemm_silu_mul(packed_codes, packed_scales, global_scale, x, h,
+                                                M, F, K, static_cast<hipStream_t>(stream)));
 }
 
 q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,

@@ -74,4 +74,21 @@ __device__ __forceinline__ float e4m3_to_f32(uint32_t w)
     return __builtin_amdgcn_cvt_f32_fp8((int)w, SEL);
 }
 
+// silu(gate) * up in fp32, rounded to bf16 (nearest even): the epilogue of
+// the fused gate/up projection
+__device__ __forceinline__ uint16_t silu_mul_bf16(float gate, float up)
+{
+    const float h = gate / (1.0f + expf(-gate)) * up;
+    return __builtin_bit_cast(uint16_t, (__bf16)h);
+}
+
+// lane r <- lane r ^ 8 within each 16-lane row (a row rotate by 8).  In a
+// fused gate/up tile lane r < 8 holds a gate output and lane r + 8 the
+// matching up output.  Every lane of the row must be active.
+__device__ __forceinline__ float swap8(float v)
+{
+    return __builtin_bit_cast(
+        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
+}
+
 }  // namespace q4p

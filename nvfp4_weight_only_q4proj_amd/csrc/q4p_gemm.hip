@@ -47,6 +47,11 @@
 //  * Dequantisation to bf16 with the e4m3 scale folded in is exact: q*s has
 //    at most 6 significant bits.  fp32 accumulation in the MFMA; y = g * acc
 //    stored once.
+//  * SILU variant (fused gate/up weight, 8 gate rows and the matching 8 up
+//    rows per 16-row tile): the lanes r and r + 8 that hold a gate/up pair
+//    swap values by a row rotate and write h = bf16(silu(g*gate) * (g*up))
+//    instead of y; lanes r < 8 take rows 4gq, 4gq+1 of each block and lanes
+//    r >= 8 rows 4gq+2, 4gq+3, so every lane evaluates two epilogues.
 #include "q4p_device.h"
 #include "q4p_launch.h"
 
@@ -101,10 +106,10 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t wd, float s)
 constexpr int kWaitVm0 = 0x0f70;
 constexpr int kWaitLgkm0 = 0xc07f;
 
-template <int Q, int RT>
+template <int Q, int RT, bool SILU>
 __global__ void __launch_bounds__(512)
 gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ pscales, float g,
-            const uint16_t *__restrict__ x, float *__restrict__ y, int M, int N, int64_t ldy,
+            const uint16_t *__restrict__ x, void *__restrict__ out, int M, int N, int64_t ldy,
             int K, int KT, int NT)
 {
     constexpr int TT = 4 * Q + RT;                         // tiles per workgroup (== T)
@@ -383,6 +388,44 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     }
 
     // ---- epilogue: lane (r, gq) holds rows 4*gq + i of each 16-row block ----
+    if (SILU) {
+        uint16_t *h = static_cast<uint16_t *>(out);
+        const bool hi = r >= 8;
+        // tile t, rows mrow + 0..3 (mrow = m0 + 16*block + 4*gq): outputs
+        // f = 8t + r%8; called with the wave's lanes all active
+        auto put = [&](int t, int mrow, const floatx4_t &v) __attribute__((always_inline)) {
+            const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+            const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
+            const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
+            const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
+            const int m = mrow + (hi ? 2 : 0);
+            const int64_t f = 8 * (int64_t)t + (r & 7);
+            if (m < M)
+                h[(int64_t)m * ldy + f] = silu_mul_bf16(g * ga, g * ua);
+            if (m + 1 < M)
+                h[(int64_t)(m + 1) * ldy + f] = silu_mul_bf16(g * gb, g * ub);
+        };
+#pragma unroll
+        for (int j = 0; j < Q; ++j) {
+            const int t = tile0 + w * Q + j;
+            if (t < NT) {
+#pragma unroll
+                for (int i = 0; i < 8; ++i)
+                    put(t, m0 + 16 * (i ^ rb) + 4 * gq, accF[j][i]);
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < RB; ++j) {
+            const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
+            if (t < NT) {
+#pragma unroll
+                for (int i = 0; i < RR; ++i)
+                    put(t, m0 + 16 * (rb + i) + 4 * gq, accR[j][i]);
+            }
+        }
+        return;
+    }
+    float *y = static_cast<float *>(out);
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
         const int t = tile0 + w * Q + j;
@@ -417,10 +460,10 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     }
 }
 
-typedef void (*gemm_fn)(const uint8_t *, const uint8_t *, float, const uint16_t *, float *, int, int,
+typedef void (*gemm_fn)(const uint8_t *, const uint8_t *, float, const uint16_t *, void *, int, int,
                         int64_t, int, int, int);
 
-#define Q4P_GEMM_ENTRY(T) gemm_kernel<(T) / 4, (T) % 4>
+#define Q4P_GEMM_ENTRY(T) gemm_kernel<(T) / 4, (T) % 4, false>
 const gemm_fn kGemmTable[kMaxT + 1] = {
     nullptr,             Q4P_GEMM_ENTRY(1),  Q4P_GEMM_ENTRY(2),  Q4P_GEMM_ENTRY(3),
     Q4P_GEMM_ENTRY(4),   Q4P_GEMM_ENTRY(5),  Q4P_GEMM_ENTRY(6),  Q4P_GEMM_ENTRY(7),
@@ -430,11 +473,20 @@ const gemm_fn kGemmTable[kMaxT + 1] = {
 };
 #undef Q4P_GEMM_ENTRY
 
-}  // namespace
+#define Q4P_GEMM_ENTRY(T) gemm_kernel<(T) / 4, (T) % 4, true>
+const gemm_fn kGemmSiluTable[kMaxT + 1] = {
+    nullptr,             Q4P_GEMM_ENTRY(1),  Q4P_GEMM_ENTRY(2),  Q4P_GEMM_ENTRY(3),
+    Q4P_GEMM_ENTRY(4),   Q4P_GEMM_ENTRY(5),  Q4P_GEMM_ENTRY(6),  Q4P_GEMM_ENTRY(7),
+    Q4P_GEMM_ENTRY(8),   Q4P_GEMM_ENTRY(9),  Q4P_GEMM_ENTRY(10), Q4P_GEMM_ENTRY(11),
+    Q4P_GEMM_ENTRY(12),  Q4P_GEMM_ENTRY(13), Q4P_GEMM_ENTRY(14), Q4P_GEMM_ENTRY(15),
+    Q4P_GEMM_ENTRY(16),  Q4P_GEMM_ENTRY(17),
+};
+#undef Q4P_GEMM_ENTRY
 
-hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
-                       const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream)
+// out: fp32 y[M][N], or with silu bf16 h[M][N/2] (N = 2F, fused gate/up)
+hipError_t launch_gemm_any(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
+                           const uint16_t *x, void *out, int64_t M, int64_t N, int64_t K,
+                           bool silu, hipStream_t stream)
 {
     const int64_t NT = n_tiles(N);
     const int64_t KT = k_tiles(K);
@@ -462,17 +514,35 @@ hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales
                 T = kMaxT;
             const int64_t NB = (NTc + T - 1) / T;
             const dim3 grid((unsigned)NB, (unsigned)MB), block(512);
-            hipLaunchKernelGGL(kGemmTable[T], grid, block, 0, stream,
+            // output columns of this chunk: 16 per tile (8 with silu)
+            void *o = silu ? static_cast<void *>(static_cast<uint16_t *>(out) + mb * (N / 2) + 8 * tb)
+                           : static_cast<void *>(static_cast<float *>(out) + mb * N + 16 * tb);
+            hipLaunchKernelGGL(silu ? kGemmSiluTable[T] : kGemmTable[T], grid, block, 0, stream,
                                packed_codes + tb * KT * kTileCodeBytes,
-                               packed_scales + tb * KT * kTileScaleBytes, g, x + mb * K,
-                               y + mb * N + 16 * tb, (int)Mc, (int)Nc, N, (int)K, (int)KT,
-                               (int)NTc);
+                               packed_scales + tb * KT * kTileScaleBytes, g, x + mb * K, o,
+                               (int)Mc, (int)Nc, silu ? N / 2 : N, (int)K, (int)KT, (int)NTc);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
         }
     }
     return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
+                       const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
+                       hipStream_t stream)
+{
+    return launch_gemm_any(packed_codes, packed_scales, g, x, y, M, N, K, false, stream);
+}
+
+hipError_t launch_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
+                                int64_t K, hipStream_t stream)
+{
+    return launch_gemm_any(packed_codes, packed_scales, g, x, h, M, 2 * F, K, true, stream);
 }
 
 }  // namespace q4p

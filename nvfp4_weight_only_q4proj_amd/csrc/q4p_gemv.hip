@@ -406,20 +406,6 @@ struct SkArgs {
     float g;
 };
 
-// silu(gate) * up in fp32, rounded to bf16 (nearest even)
-__device__ __forceinline__ uint16_t silu_mul_bf16(float gate, float up)
-{
-    const float h = gate / (1.0f + expf(-gate)) * up;
-    return __builtin_bit_cast(uint16_t, (__bf16)h);
-}
-
-// lane r <- lane r ^ 8 within each 16-lane row (a row rotate by 8)
-__device__ __forceinline__ float swap8(float v)
-{
-    return __builtin_bit_cast(
-        float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), 0x128, 0xF, 0xF, false));
-}
-
 // A gate/up pair of partial sums in one 64-bit exchange word.  Both fields
 // are XORed with a NaN pattern that no stored value has (a NaN is stored as
 // the one canonical quiet NaN), so a word holding a pair is never zero and

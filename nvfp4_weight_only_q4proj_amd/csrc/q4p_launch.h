@@ -36,4 +36,9 @@ hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);
 
+// The fused gate/up projection + silu(gate)*up for any M (F % 8 == 0).
+hipError_t launch_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
+                                int64_t K, hipStream_t stream);
+
 }  // namespace q4p

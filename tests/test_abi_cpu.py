@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(q4):
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     lib = q4.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -148,22 +148,26 @@ def test_gemv_m_range(q4):
     assert proj(lib, "q4proj_gemv", M=1000) == q4.EUNSUPPORTED
 
 
-def silu(lib, pc=A, ps=B, x=X, h=Y, M=1, F=64, K=256, ws=W, wsb=WSB):
-    return lib.q4proj_gemv_silu_mul(pc, ps, ctypes.c_float(1.0), x, h, M, F, K, ws, wsb, None)
+def silu(lib, pc=A, ps=B, x=X, h=Y, M=1, F=64, K=256, ws=W, wsb=WSB, fn="q4proj_gemv_silu_mul"):
+    return getattr(lib, fn)(pc, ps, ctypes.c_float(1.0), x, h, M, F, K, ws, wsb, None)
+
+
+SILU_BAD = [dict(pc=None), dict(ps=None), dict(x=None), dict(h=None), dict(M=0), dict(F=0),
+            dict(F=12), dict(F=-16), dict(K=0), dict(K=24), dict(x=X + 8), dict(pc=A + 4),
+            dict(ps=B + 4), dict(h=Y + 1), dict(h=X + 64), dict(h=A), dict(M=-1)]
 
 
 def test_silu_mul_validation(q4):
     lib = q4.library()
     assert q4.q4proj_silu_mul_workspace_bytes(1, 64, 256) == WSB
-    for kw in [dict(pc=None), dict(ps=None), dict(x=None), dict(h=None), dict(M=0), dict(F=0),
-               dict(F=12), dict(F=-16), dict(K=0), dict(K=24), dict(x=X + 8), dict(pc=A + 4),
-               dict(ps=B + 4), dict(h=Y + 1), dict(h=X + 64), dict(h=A), dict(ws=None),
-               dict(ws=W + 4), dict(ws=Y - 4096), dict(ws=X)]:
+    for kw in SILU_BAD + [dict(ws=None), dict(ws=W + 4), dict(ws=Y - 4096), dict(ws=X)]:
         assert silu(lib, **kw) == q4.EINVAL, kw
     assert silu(lib, M=17) == q4.EUNSUPPORTED
     assert silu(lib, M=16, K=32768 + 128) == q4.EUNSUPPORTED
     assert silu(lib, wsb=WSB - 8) == q4.EWORKSPACE
     assert silu(lib, ws=None, wsb=0) == q4.EWORKSPACE
+    for kw in SILU_BAD:
+        assert silu(lib, **{"fn": "q4proj_gemm_silu_mul", "M": 512, **kw}) == q4.EINVAL, kw
 
 
 @pytest.mark.parametrize("fn", ["q4proj_pack", "q4proj_unpack"])
@@ -196,3 +200,4 @@ def test_no_device_no_fallback(q4):
     assert lib.q4proj_pack(A, B, 16, 128, X, Y, None) == q4.EDEVICE
     assert silu(lib) == q4.EDEVICE
     assert silu(lib, h=Y + 2) == q4.EDEVICE             # bf16 out needs 2-byte alignment only
+    assert silu(lib, fn="q4proj_gemm_silu_mul", M=512, ws=None, wsb=0) == q4.EDEVICE

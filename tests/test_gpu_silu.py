@@ -1,5 +1,5 @@
-"""q4proj_gemv_silu_mul (fused gate/up projection + silu(gate)*up, bf16 out)
-against the CPU oracle.
+"""q4proj_gemv_silu_mul and q4proj_gemm_silu_mul (fused gate/up projection +
+silu(gate)*up, bf16 out) against the CPU oracle.
 
 * small and ragged shapes on every output, including shapes whose waves hold
   many whole tiles, tiles shared by waves and workgroups (pairs exchanged in
@@ -26,11 +26,12 @@ def fused_matrix(seed, F, K):
     return synth.nvfp4_normal_matrix(seed, 1, 2 * F, K)
 
 
-def run_fused(packed, g, x, F, K, workspace=None):
+def run_fused(packed, g, x, F, K, workspace=None, kind="gemv"):
     m = q4()
     M = x.shape[0]
     h = torch.full((M, F), -1, dtype=torch.int16, device=DEV)     # bf16 NaN pattern 0xFFFF
-    m.q4proj_gemv_silu_mul(packed[0], packed[1], g, to_dev_x(x), h, M, F, K, workspace=workspace)
+    fn = m.q4proj_gemv_silu_mul if kind == "gemv" else m.q4proj_gemm_silu_mul
+    fn(packed[0], packed[1], g, to_dev_x(x), h, M, F, K, workspace=workspace)
     torch.cuda.synchronize()
     return h.cpu().numpy().view(np.uint16)
 
@@ -154,3 +155,76 @@ def test_rejects_what_it_does_not_serve():
     assert call(1, 12, 128) == m.EINVAL
     assert call(17, 16, 128) == m.EUNSUPPORTED
     assert call(16, 16, 32896) == m.EUNSUPPORTED
+
+
+# ---- the matrix-core path (any M) ------------------------------------------
+
+GEMM_SMALL = [(M, F, K) for M in (1, 33, 200) for F in (8, 40, 272) for K in (16, 208, 1040)]
+
+
+@pytest.mark.parametrize("M,F,K", GEMM_SMALL)
+def test_gemm_small_shapes(M, F, K):
+    mat = fused_matrix(80 + M, F, K)
+    x = synth.x_bf16(80, M, M, K)
+    note(f"gemm_silu_mul M={M} F={F} K={K}")
+    h = run_fused(pack(mat.codes, mat.scales, 2 * F, K), mat.g, x, F, K, kind="gemm")
+    assert_silu_parity(mat, x, F, h)
+
+
+# M = 512 with 3, 6, 9, 16 and 17 tiles per workgroup (every split of the
+# tiles between the four wave pairs), on sampled outputs of every row
+GEMM_TILINGS = [(1096, 256), (2816, 256), (4352, 128), (8192, 128), (17408, 5120)]
+
+
+@pytest.mark.parametrize("F,K", GEMM_TILINGS)
+def test_gemm_prefill_tilings(F, K):
+    M = 512
+    if F == 17408:
+        (c,) = synth.workload_cases("pre", only=["gate_up"])
+        x = c.x
+        mat = synth.workload_cases("mlp")[0].matrix
+    else:
+        mat = fused_matrix(90, F, K)
+        x = synth.x_bf16(90, 1, M, K)
+    packed = pack(mat.codes, mat.scales, 2 * F, K)
+    note(f"gemm_silu_mul M={M} F={F} K={K}")
+    h1 = run_fused(packed, mat.g, x, F, K, kind="gemm")
+    h2 = run_fused(packed, mat.g, x, F, K, kind="gemm")
+    assert np.array_equal(h1, h2)
+    cols = sample_cols(F, 256, F)
+    worst = assert_silu_parity(mat, x, F, h1, cols)
+    print(f"fused gate/up gemm F={F} K={K}: worst |h-h_ref|/allowance = {worst:.3g}")
+
+
+@pytest.mark.parametrize("M,F,K", [(512, 4352, 1040), (77, 2048, 5120)])
+def test_gemm_matches_unfused(M, F, K):
+    mat = fused_matrix(100, F, K)
+    x = synth.x_bf16(100, M, M, K)
+    packed = pack(mat.codes, mat.scales, 2 * F, K)
+    note(f"gemm_silu_mul vs gemm M={M} F={F} K={K}")
+    h = run_fused(packed, mat.g, x, F, K, kind="gemm")
+    y = torch.empty((M, 2 * F), dtype=torch.float32, device=DEV)
+    q4().q4proj_gemm(packed[0], packed[1], mat.g, to_dev_x(x), y, M, 2 * F, K)
+    torch.cuda.synchronize()
+    y = y.cpu().numpy().astype(np.float64)
+    grow, urow = oracle.gate_up_rows(F)
+    want = bf16_round(oracle.silu_mul(y[:, grow], y[:, urow]))
+    diff = np.abs(h.astype(np.int32) - want.astype(np.int32))
+    assert diff.max() <= 1
+    assert np.mean(diff == 0) > 0.995
+
+
+def test_gemm_nan_scale_poisons_its_pair():
+    F, K, M = 64, 256, 40
+    mat = fused_matrix(70, F, K)
+    scales = mat.scales.copy()
+    scales[32 + 5, 3] = 0x7F              # fused row 37 = gate row of output f = 21
+    scales[16 + 8 + 1, 0] = 0xFF          # fused row 25 = up row of output f = 9
+    x = synth.x_bf16(71, M, M, K)
+    note("gemm_silu_mul NaN scales")
+    h = run_fused(pack(mat.codes, scales, 2 * F, K), mat.g, x, F, K, kind="gemm")
+    nan = (h & 0x7FFF) > 0x7F80
+    assert nan[:, [9, 21]].all() and nan.sum() == 2 * M
+    bad, _ = oracle.check_bf16(*oracle.silu_mul_cols(mat.codes, scales, mat.g, x, F), h)
+    assert bad == 0
+
