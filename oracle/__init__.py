@@ -11,6 +11,8 @@ with gcc into ``liboracle.so`` and exposes numpy-level wrappers:
 * :func:`dequant_row` — one weight row in fp64,
 * :func:`proj` / :func:`proj_rows` — y and the tolerance base S in fp64,
 * :func:`check` — the acceptance test |y_gpu - y_ref| <= rtol * S,
+* :func:`quantize` / :func:`quant_global_scale` — the NVFP4 quantizer
+  (bf16 weights -> codes, e4m3 block scales, global scale), decisions in fp32,
 * :func:`silu_mul_cols` / :func:`check_bf16` — the fused gate/up projection
   h = silu(gate) * up on a weight whose gate and up rows are interleaved in
   groups of 8, its error allowance, and the bf16 acceptance test.
@@ -75,6 +77,14 @@ def load(path: str = LIB):
     lib.orc_silu_mul_bound.restype = None
     lib.orc_check_bf16.argtypes = [i64, vp, vp, vp, ctypes.POINTER(dbl)]
     lib.orc_check_bf16.restype = i64
+    lib.orc_quant_e4m3.argtypes = [ctypes.c_float]
+    lib.orc_quant_e4m3.restype = ctypes.c_uint
+    lib.orc_quant_e2m1.argtypes = [ctypes.c_float]
+    lib.orc_quant_e2m1.restype = ctypes.c_uint
+    lib.orc_quant_global_scale.argtypes = [i64, vp]
+    lib.orc_quant_global_scale.restype = ctypes.c_float
+    lib.orc_quantize.argtypes = [i64, i64, vp, ctypes.c_float, vp, vp]
+    lib.orc_quantize.restype = None
     if path == LIB:
         _lib = lib
     return lib
@@ -207,3 +217,27 @@ def check_bf16(h_ref, bound, h_gpu_bits, lib=None):
     worst = ctypes.c_double(0.0)
     bad = (lib or load()).orc_check_bf16(hr.size, _ptr(hr), _ptr(bd), _ptr(hg), ctypes.byref(worst))
     return int(bad), float(worst.value)
+
+
+def quant_global_scale(w_bits, lib=None) -> float:
+    """g = amax / 2688 in fp32 (1 for an all-zero tensor) of bf16 bit patterns."""
+    w = _as_u16(w_bits)
+    return float((lib or load()).orc_quant_global_scale(w.size, _ptr(w)))
+
+
+def quantize(w_bits, N: int, K: int, g=None, rows=None, lib=None):
+    """Quantise bf16 W [N][K] (bit patterns) -> (codes u8 [R][K/2], scales u8
+    [R][K/16], g) for rows `rows` (default all; R = len(rows)).  g defaults to
+    the tensor's global scale."""
+    lib = lib or load()
+    w = _as_u16(w_bits).reshape(N, K)
+    if g is None:
+        g = quant_global_scale(w, lib)
+    if rows is not None:
+        w = np.ascontiguousarray(w[np.asarray(rows, dtype=np.int64)])
+    R = w.shape[0]
+    codes = np.empty((R, K // 2), dtype=np.uint8)
+    scales = np.empty((R, K // 16), dtype=np.uint8)
+    lib.orc_quantize(R, K, _ptr(w), float(g), _ptr(codes), _ptr(scales))
+    return codes, scales, float(g)
+

@@ -324,3 +324,125 @@ int64_t orc_check_bf16(int64_t count, const double *href, const double *bound,
         *max_ratio = worst;
     return bad;
 }
+
+/* ---- the NVFP4 quantizer: bf16 W -> (codes, e4m3 block scales, g) ---------
+ *
+ * The FlashRT "Qwen3.6 NVFP4 usage" page (environment-variable table, the MTP
+ * checkpoint entry) converts weights to NVFP4 at load time (FP8 -> BF16 ->
+ * NVFP4).  The page gives no formula; the reading here is the two-level
+ * NVFP4 recipe: a per-tensor fp32 global scale that maps the tensor's largest
+ * magnitude to the largest representable product 6 * 448, an e4m3 scale per
+ * 16 consecutive k that maps the block's largest magnitude to the largest
+ * e2m1 magnitude 6, and each element rounded to the nearest e2m1 value.
+ *
+ * The rounding decisions are taken in fp32 with IEEE round-to-nearest
+ * operations, in this order (the kernel's precision, so both sides decide
+ * alike):
+ *     amax = max |w|                       (exact; bf16 values)
+ *     g    = amax / 2688                    (g = 1 when amax == 0)
+ *   per 16-element block b:
+ *     t    = (amax_b / 6) / g
+ *     s_b  = the e4m3 code nearest to t, ties to the even code, t beyond
+ *            448 saturating to 448 (code 0x7E)
+ *     unit = e4m3(s_b) * g,   inv = 1 / unit
+ *   per element:
+ *     r    = |w| * inv
+ *     code = the e2m1 magnitude code nearest to r, ties to the even code,
+ *            r beyond 6 saturating to 6 (code 7), NaN (0 * inf) giving 0;
+ *            bit 3 = the sign bit of w
+ *   and every code of a block is 0 when unit == 0.
+ * "Nearest" is found by searching the decoded code values (orc_e2m1,
+ * orc_e4m3) in fp64, where the distances are exact.
+ */
+
+/* nearest e4m3 code in 0..0x7E to t >= 0 (ties to the even code) */
+static unsigned quant_e4m3(float t)
+{
+    if (t > 448.0f)
+        return 0x7Eu;
+    unsigned best = 0;
+    double bd = INFINITY;
+    for (unsigned c = 0; c <= 0x7Eu; ++c) {
+        const double d = fabs((double)t - orc_e4m3(c));
+        if (d < bd || (d == bd && (c & 1u) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return best;
+}
+
+/* nearest e2m1 magnitude code in 0..7 to r >= 0 (ties to the even code) */
+static unsigned quant_e2m1(float r)
+{
+    if (isnan(r))
+        return 0u;
+    if (r > 6.0f)
+        return 7u;
+    unsigned best = 0;
+    double bd = INFINITY;
+    for (unsigned c = 0; c <= 7u; ++c) {
+        const double d = fabs((double)r - orc_e2m1(c));
+        if (d < bd || (d == bd && (c & 1u) == 0)) {
+            best = c;
+            bd = d;
+        }
+    }
+    return best;
+}
+
+/* single-value forms of the two rounding steps (for the tests) */
+unsigned orc_quant_e4m3(float t) { return quant_e4m3(t); }
+unsigned orc_quant_e2m1(float r) { return quant_e2m1(r); }
+
+static float bf16_to_float(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* The global scale of a bf16 tensor of `count` elements. */
+float orc_quant_global_scale(int64_t count, const uint16_t *w)
+{
+    float amax = 0.0f;
+    for (int64_t i = 0; i < count; ++i) {
+        const float a = fabsf(bf16_to_float(w[i]));
+        if (a > amax)
+            amax = a;
+    }
+    return amax == 0.0f ? 1.0f : amax / 2688.0f;
+}
+
+/* Quantise rows of w (bf16 [N][K], K % 16 == 0) with global scale g into
+ * canonical codes [N][K/2] and scales [N][K/16]. */
+void orc_quantize(int64_t N, int64_t K, const uint16_t *w, float g, uint8_t *codes,
+                  uint8_t *scales)
+{
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t b = 0; b < K / 16; ++b) {
+            const uint16_t *wb = w + n * K + 16 * b;
+            float amax_b = 0.0f;
+            for (int i = 0; i < 16; ++i) {
+                const float a = fabsf(bf16_to_float(wb[i]));
+                if (a > amax_b)
+                    amax_b = a;
+            }
+            const float t = (amax_b / 6.0f) / g;
+            const unsigned s = quant_e4m3(t);
+            const float unit = (float)orc_e4m3(s) * g;
+            const float inv = 1.0f / unit;
+            scales[n * (K / 16) + b] = (uint8_t)s;
+            for (int i = 0; i < 16; i += 2) {
+                unsigned q[2];
+                for (int j = 0; j < 2; ++j) {
+                    const uint16_t bits = wb[i + j];
+                    const float r = fabsf(bf16_to_float(bits)) * inv;
+                    q[j] = unit == 0.0f ? 0u : quant_e2m1(r) | ((bits >> 15) << 3);
+                }
+                codes[n * (K / 2) + 8 * b + i / 2] = (uint8_t)(q[0] | (q[1] << 4));
+            }
+        }
+    }
+}

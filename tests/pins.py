@@ -385,7 +385,141 @@ def pin_silu_mul_bound(lib):
         assert bad == 1, (i, v, bad)
 
 
+# ---- the NVFP4 quantizer ----------------------------------------------------
+
+def golden_e2m1_rounding():
+    rows = []
+    for line in open(os.path.join(GOLDEN, "e2m1_rne_ocp_mx_v1.txt")):
+        if line.strip() and not line.startswith("#"):
+            v, c = line.split()
+            rows.append((float(v), int(c, 16)))
+    return rows
+
+
+def pin_quant_e2m1_rounding(lib):
+    """e2m1 rounding against the OCP MX conversion rule, tabulated."""
+    rows = golden_e2m1_rounding()
+    assert len(rows) >= 20
+    for v, c in rows:
+        assert lib.orc_quant_e2m1(v) == c, (v, c, lib.orc_quant_e2m1(v))
+    assert lib.orc_quant_e2m1(float("inf")) == 7
+
+
+def pin_quant_e4m3_torch(lib):
+    """e4m3 rounding against torch's float8_e4m3fn cast (round to nearest
+    even) on every value, every midpoint between neighbours, one fp32 ulp to
+    each side of every midpoint, and random values in [0, 448]; saturation
+    above 448 in closed form."""
+    vals = pins_e4m3_positive()
+    mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
+    assert np.array_equal(mids.astype(np.float64), (vals[:-1].astype(np.float64) + vals[1:]) / 2)
+    rng = np.random.default_rng(9)
+    t = np.concatenate([vals, mids, np.nextafter(mids, np.float32(0)),
+                        np.nextafter(mids, np.float32(np.inf)),
+                        rng.uniform(0, 448, 3000).astype(np.float32),
+                        (2.0 ** rng.uniform(-12, -5, 1000)).astype(np.float32)])
+    want = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    got = np.array([lib.orc_quant_e4m3(float(v)) for v in t])
+    assert np.array_equal(got, want), t[got != want][:5]
+    for v in (448.0001, 460.0, 464.0, 1e6, float("inf")):
+        assert lib.orc_quant_e4m3(v) == 0x7E
+
+
+def pins_e4m3_positive():
+    """The 127 non-negative finite e4m3 values in code order (torch's decoder)."""
+    return torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+
+
+def pin_quant_global_scale(lib):
+    """g = amax / 2688 as one fp32 division (numpy's IEEE float32), 1 for an
+    all-zero tensor (also of negative zeros)."""
+    rng = np.random.default_rng(10)
+    for scale in (0.02, 3e-39, 1e30):
+        w = torch.from_numpy(rng.normal(0, 1, 4096) * scale).to(torch.bfloat16)
+        bits = w.view(torch.int16).numpy().view(np.uint16)
+        amax = np.float32(np.abs(w.float().numpy()).max())
+        assert oracle.quant_global_scale(bits, lib) == np.float32(amax) / np.float32(2688)
+    assert oracle.quant_global_scale(np.zeros(64, np.uint16), lib) == 1.0
+    assert oracle.quant_global_scale(np.full(64, 0x8000, np.uint16), lib) == 1.0
+
+
+def pin_quantize_exact_recovery(lib):
+    """Weights that are exactly q * s * g, every block holding a +-6 element
+    and one block the scale 448 (so the tensor's amax is 2688 g), come back
+    as the same codes and scales."""
+    rng = np.random.default_rng(11)
+    N, K = 12, 256
+    g = 2.0 ** -14
+    e4 = pins_e4m3_positive()
+    e2 = np.array([lib.orc_e2m1(c) for c in range(16)])
+    s = rng.integers(0x08, 0x7F, (N, K // 16)).astype(np.uint8)      # normal scales
+    s[3, 5] = 0x7E
+    q = rng.integers(0, 16, (N, K)).astype(np.uint8)
+    q[:, ::16] = rng.choice([7, 15], (N, K // 16))                      # one +-6 per block
+    w = e2[q] * np.repeat(e4[s].astype(np.float64), 16, axis=1) * g
+    bits = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(pins_bf16_of(bits), w)                        # exact in bf16
+    codes, scales, gq = oracle.quantize(bits, N, K, lib=lib)
+    assert gq == g
+    assert np.array_equal(scales, s)
+    assert np.array_equal(codes, (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8))
+
+
+def pins_bf16_of(bits):
+    return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+
+
+def _nearest_ok(x, grid, chosen, rel=2.0 ** -20):
+    """chosen is the grid value nearest to x, or x lies within rel of the
+    midpoint between chosen and the nearest value (fp32 decisions on x)."""
+    d = np.abs(grid[None, :] - x[:, None])
+    best = d.min(axis=1)
+    dc = np.abs(chosen - x)
+    return (dc <= best) | (np.abs(dc - best) <= rel * np.maximum(np.abs(x), 1e-300))
+
+
+def pin_quantize_nearest(lib):
+    """Every scale is the e4m3 value nearest to (amax_b / 6) / g and every
+    code the e2m1 magnitude nearest to |w| / (s g) (beyond 6: 6), with the
+    sign of w, checked in fp64; zero blocks give scale 0 and codes 0; tiny
+    blocks give subnormal or zero scales."""
+    rng = np.random.default_rng(12)
+    N, K = 24, 512
+    w = rng.normal(0, 0.02, (N, K))
+    w[2] = 0.0
+    w[3, :64] = 0.0
+    w[4, :256] *= 1e-4                             # subnormal e4m3 scales
+    w[4, 256:] *= 1e-6                             # zero e4m3 scales
+    w[5, 7] = 0.9                                  # the tensor's amax
+    w[6, ::3] = -0.0
+    bits = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    wv = pins_bf16_of(bits).reshape(N, K)
+    codes, scales, g = oracle.quantize(bits, N, K, lib=lib)
+    e4 = pins_e4m3_positive().astype(np.float64)
+    e2 = np.array([lib.orc_e2m1(c) for c in range(8)])
+    amax_b = np.abs(wv).reshape(N, K // 16, 16).max(axis=2)
+    t = (amax_b / 6.0 / g).ravel()
+    sv = e4[scales.ravel()]
+    assert _nearest_ok(np.minimum(t, 448.0), e4, sv).all()
+    assert (scales[2] == 0).all() and (scales[3, :4] == 0).all()
+    assert (scales[4] < 0x08).any() and (scales[4] == 0).any()
+    q = np.empty((N, K), np.uint8)
+    q[:, 0::2] = codes & 15
+    q[:, 1::2] = codes >> 4
+    unit = np.repeat(e4[scales].astype(np.float64) * g, 16, axis=1)
+    live = unit > 0
+    r = np.where(live, np.abs(wv) / np.where(live, unit, 1.0), 0.0)
+    mag = e2[q & 7]
+    ok = _nearest_ok(np.minimum(r[live], 6.0), e2, mag[live])
+    assert ok.all(), np.argwhere(~ok)[:5]
+    assert (q[~live] == 0).all()
+    neg = (bits.reshape(N, K) >> 15) == 1
+    assert ((q[live] >> 3) == neg[live]).all()
+
+
 ALL_PINS = [pin_e2m1_table, pin_e4m3_torch, pin_e4m3_landmarks, pin_bf16_torch,
             pin_dequant_rows, pin_exact_tiny_fast, pin_abs_sum, pin_one_hot,
             pin_invariants, pin_nan_scale, pin_check, pin_silu_mul_torch,
-            pin_silu_mul_fused_rows, pin_silu_mul_bound]
+            pin_silu_mul_fused_rows, pin_silu_mul_bound, pin_quant_e2m1_rounding,
+            pin_quant_e4m3_torch, pin_quant_global_scale, pin_quantize_exact_recovery,
+            pin_quantize_nearest]

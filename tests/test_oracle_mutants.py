@@ -48,6 +48,21 @@ MUTANTS = {
     "silu_bound_slope": ("bound[i] = 1.1 * da", "bound[i] = 0.5 * da", 1),
     "silu_bound_up_term": ("+ fabs(sg) * db;", ";", 1),
     "check_bf16_rounding": ("ldexp(fabs(r) + bound[i], -8)", "ldexp(fabs(r) + bound[i], -4)", 1),
+    "quant_global_448": ("amax / 2688.0f", "amax / 448.0f", 1),
+    "quant_zero_global": ("return amax == 0.0f ? 1.0f :", "return amax == 0.0f ? 0.0f :", 1),
+    "quant_block_div4": ("(amax_b / 6.0f) / g", "(amax_b / 4.0f) / g", 1),
+    "quant_e4m3_ties_odd": ("orc_e4m3(c));\n        if (d < bd || (d == bd && (c & 1u) == 0)) {",
+                            "orc_e4m3(c));\n        if (d < bd || (d == bd && (c & 1u) == 1)) {", 1),
+    "quant_e2m1_ties_odd": ("orc_e2m1(c));\n        if (d < bd || (d == bd && (c & 1u) == 0)) {",
+                            "orc_e2m1(c));\n        if (d < bd || (d == bd && (c & 1u) == 1)) {", 1),
+    "quant_e2m1_ties_up": ("orc_e2m1(c));\n        if (d < bd || (d == bd && (c & 1u) == 0)) {",
+                           "orc_e2m1(c));\n        if (d <= bd) {", 1),
+    "quant_e4m3_not_saturating": ("if (t > 448.0f)\n        return 0x7Eu;", "if (t > 448.0f)\n        return 0x7Fu;", 1),
+    "quant_e2m1_not_saturating": ("if (r > 6.0f)\n        return 7u;", "if (r > 6.0f)\n        return 6u;", 1),
+    "quant_sign_dropped": ("quant_e2m1(r) | ((bits >> 15) << 3)", "quant_e2m1(r)", 1),
+    "quant_unit_without_g": ("(float)orc_e4m3(s) * g;", "(float)orc_e4m3(s);", 1),
+    "quant_nibbles_swapped": ("(uint8_t)(q[0] | (q[1] << 4))", "(uint8_t)(q[1] | (q[0] << 4))", 1),
+    "quant_block_amax_first": ("if (a > amax_b)\n                    amax_b = a;", "if (i == 0)\n                    amax_b = a;", 1),
 }
 
 
