@@ -26,6 +26,10 @@ Also measured and reported in the same JSON line:
                 each beside the plain projection over the same packed weight
                 (fp32 out, no epilogue).
   pack          the one-time weight swizzle (read + write bytes / s).
+  quantize      the load-time NVFP4 conversion of bf16 weights (fused gate/up
+                34816 x 5120 and lm-head 248320 x 5120): algorithmic bytes
+                (bf16 in, codes + scales out) / s; two launches, the first
+                reads w for its max, the second reads it again to quantize.
   cpu_baseline  the CPU oracle on the decode step, on the host cores.
 """
 from __future__ import annotations
@@ -109,7 +113,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="wall-time bound of the cpu_baseline sample")
-    ap.add_argument("--only", choices=["dec", "pre", "mlp", "all"], default="all",
+    ap.add_argument("--only", choices=["dec", "pre", "mlp", "quant", "all"], default="all",
                     help="restrict the run (for profiling one kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
@@ -334,6 +338,34 @@ def main():
             "per_M": fused,
             "kernel_source_sha256_16": {"gemv": src_digest("q4p_gemv.hip"),
                                         "gemm": src_digest("q4p_gemm.hip")}}
+
+    # ---- NVFP4 quantizer --------------------------------------------------
+    if args.only in ("quant", "all"):
+        quant = {}
+        gen = torch.Generator(device=dev)
+        for name, N, K in (("gate_up_fused", 34816, 5120), ("lm_head", 248320, 5120)):
+            gen.manual_seed(6)
+            w = (torch.randn(N * K, generator=gen, device=dev) * 0.02).to(torch.bfloat16)
+            codes = torch.empty(N * K // 2, dtype=torch.uint8, device=dev)
+            scales = torch.empty(N * K // 16, dtype=torch.uint8, device=dev)
+            gq = torch.empty(1, dtype=torch.float32, device=dev)
+            ws = torch.empty(q4.q4proj_quantize_workspace_bytes(N, K), dtype=torch.uint8,
+                             device=dev)
+            run = lambda: q4.q4proj_quantize(w, N, K, codes, scales, gq, workspace=ws)
+            for _ in range(2):
+                run()
+            n = 5
+            ms, _ = timed_region(torch, [run] * n, n)
+            b = 2 * N * K + N * K // 2 + N * K // 16 + 4
+            quant[name] = {"N": N, "K": K, "us": round(ms * 1e3, 1),
+                           "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                           "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                           "read_bytes_per_weight": 4, "algorithmic_bytes": b}
+            del w, codes, scales, gq, ws
+        out["quantize"] = {"workload": "bf16 -> NVFP4 (codes, e4m3 scales, g), synthetic "
+                                       "N(0, 0.02) weights", "per_matrix": quant,
+                           "kernels": ["quant_amax_kernel", "quant_kernel"],
+                           "kernel_source_sha256_16": src_digest("q4p_quant.hip")}
 
     if args.calibrate_copy:
         a = torch.empty(256 << 20, dtype=torch.uint8, device=dev)

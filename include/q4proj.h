@@ -204,6 +204,39 @@ q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                    int64_t M, int64_t F, int64_t K, void *workspace,
                                    size_t workspace_bytes, void *stream);
 
+/*
+ * Device scratch q4proj_quantize needs: 4096 bytes for every valid (N, K),
+ * 0 otherwise.  No initial contents are required and none are kept between
+ * calls; calls that may run at the same time need separate workspaces.
+ */
+size_t q4proj_quantize_workspace_bytes(int64_t N, int64_t K);
+
+/*
+ * q4proj_quantize — the load-time NVFP4 conversion of a bf16 weight (the
+ * FlashRT "Qwen3.6 NVFP4 usage" page converts its MTP checkpoint FP8 ->
+ * BF16 -> NVFP4 when the runner is constructed), producing the canonical
+ * codes and scales that q4proj_pack takes, and the global scale.
+ * In:  w       uint16 [N][K] bf16 bit patterns, finite, 16-byte aligned.
+ * Out: codes   uint8 [N][K/2] (element 2j in the low nibble), 8-byte aligned
+ *      scales  uint8 [N][K/16] e4m3
+ *      global_scale  one float in DEVICE memory (copy it to the host once to
+ *      pass it by value to the projections).
+ * Two-level recipe, each step one IEEE fp32 operation in this order:
+ *      amax = max |w|;  g = amax / 2688 (6 * 448; g = 1 when amax == 0)
+ *      per 16-element block: t = (amax_b / 6) / g; s = the e4m3 value
+ *      nearest to t, ties to the even code, saturating at 448;
+ *      inv = 1 / (s * g)
+ *      per element: the e2m1 magnitude nearest to |w| * inv, ties to the even
+ *      code, saturating at 6; the code's sign bit is w's sign bit; a block
+ *      with s * g == 0 gets all-zero codes.
+ * Deterministic.  The result for non-finite w is unspecified (no fault).
+ * Errors: EINVAL (null pointer, N/K <= 0, K % 16 != 0, misaligned w or
+ *         codes, overlapping buffers), EWORKSPACE, EDEVICE, EHIP.
+ */
+q4proj_status q4proj_quantize(const uint16_t *w, int64_t N, int64_t K, uint8_t *codes,
+                              uint8_t *scales, float *global_scale, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
 /* Human-readable name of a status code (static storage, never NULL). */
 const char *q4proj_status_string(q4proj_status s);
 

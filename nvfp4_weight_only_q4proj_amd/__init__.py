@@ -52,6 +52,10 @@ _lib.q4proj_gemv_silu_mul.argtypes = _PROJ_ARGS
 _lib.q4proj_gemv_silu_mul.restype = ctypes.c_int
 _lib.q4proj_gemm_silu_mul.argtypes = _PROJ_ARGS
 _lib.q4proj_gemm_silu_mul.restype = ctypes.c_int
+_lib.q4proj_quantize_workspace_bytes.argtypes = [_i64, _i64]
+_lib.q4proj_quantize_workspace_bytes.restype = _sz
+_lib.q4proj_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.q4proj_quantize.restype = ctypes.c_int
 _lib.q4proj_status_string.argtypes = [ctypes.c_int]
 _lib.q4proj_status_string.restype = ctypes.c_char_p
 _lib.q4proj_last_hip_error.argtypes = []
@@ -61,6 +65,7 @@ _lib.q4proj_last_hip_error.restype = ctypes.c_char_p
 SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
            "q4proj_pack", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
            "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul", "q4proj_gemm_silu_mul",
+           "q4proj_quantize_workspace_bytes", "q4proj_quantize",
            "q4proj_status_string", "q4proj_last_hip_error")
 
 OK, EINVAL, EUNSUPPORTED, EDEVICE, EWORKSPACE, EHIP = range(6)
@@ -243,6 +248,41 @@ def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, 
         _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
                   x.data_ptr(), h.data_ptr(), M, F, K, ws_ptr, ws_bytes, _stream(x, stream)),
                where)
+
+
+def q4proj_quantize_workspace_bytes(N: int, K: int) -> int:
+    return int(_lib.q4proj_quantize_workspace_bytes(N, K))
+
+
+def q4proj_quantize(w, N: int, K: int, codes: torch.Tensor, scales: torch.Tensor,
+                    global_scale: torch.Tensor, workspace=None, stream=None) -> None:
+    """bf16 w [N][K] -> codes u8 [N][K/2], scales u8 [N][K/16], global_scale
+    (a one-element float32 device tensor)."""
+    w = _bf16_bits(w, "w")
+    dev = w.device
+    _need(w, "w", w.dtype, N * K, dev)
+    _need(codes, "codes", torch.uint8, N * (K // 2), dev)
+    _need(scales, "scales", torch.uint8, N * (K // 16), dev)
+    _need(global_scale, "global_scale", torch.float32, 1, dev)
+    if workspace is None:
+        workspace = torch.empty(q4proj_quantize_workspace_bytes(N, K), dtype=torch.uint8,
+                                device=dev)
+    _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
+    with torch.cuda.device(dev):
+        _check(_lib.q4proj_quantize(w.data_ptr(), N, K, codes.data_ptr(), scales.data_ptr(),
+                                    global_scale.data_ptr(), workspace.data_ptr(),
+                                    workspace.numel(), _stream(w, stream)), "q4proj_quantize")
+
+
+def quantize_weight(w, N: int, K: int, stream=None):
+    """Allocate canonical codes/scales and a device global scale on w.device
+    and fill them with q4proj_quantize."""
+    dev = w.device
+    codes = torch.empty(N * (K // 2), dtype=torch.uint8, device=dev)
+    scales = torch.empty(N * (K // 16), dtype=torch.uint8, device=dev)
+    g = torch.empty(1, dtype=torch.float32, device=dev)
+    q4proj_quantize(w, N, K, codes, scales, g, stream=stream)
+    return codes, scales, g
 
 
 def pack_weight(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, stream=None):

@@ -18,7 +18,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libq4proj.so")
 
-HIP_SOURCES = ["q4p_pack.hip", "q4p_gemv.hip", "q4p_gemm.hip"]
+HIP_SOURCES = ["q4p_pack.hip", "q4p_gemv.hip", "q4p_gemm.hip", "q4p_quant.hip"]
 HOST_SOURCES = ["q4p_api.cpp"]
 ARCH = "gfx950"
 

@@ -254,6 +254,40 @@ q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                                 M, F, K, static_cast<hipStream_t>(stream)));
 }
 
+size_t q4proj_quantize_workspace_bytes(int64_t N, int64_t K)
+{
+    return shape_ok(N, K) ? q4p::quant_workspace_bytes() : 0;
+}
+
+q4proj_status q4proj_quantize(const uint16_t *w, int64_t N, int64_t K, uint8_t *codes,
+                              uint8_t *scales, float *global_scale, void *workspace,
+                              size_t workspace_bytes, void *stream)
+{
+    if (!w || !codes || !scales || !global_scale || !shape_ok(N, K))
+        return Q4P_EINVAL;
+    if (!aligned(w, 16) || !aligned(codes, 8) || !aligned(global_scale, 4))
+        return Q4P_EINVAL;
+    const size_t wb = (size_t)N * (size_t)K * 2, cb = (size_t)N * (size_t)(K / 2),
+                 sb = (size_t)N * (size_t)(K / 16);
+    if (overlap(codes, cb, w, wb) || overlap(scales, sb, w, wb) || overlap(codes, cb, scales, sb) ||
+        overlap(global_scale, 4, w, wb) || overlap(global_scale, 4, codes, cb) ||
+        overlap(global_scale, 4, scales, sb))
+        return Q4P_EINVAL;
+    const size_t need = q4proj_quantize_workspace_bytes(N, K);
+    if (workspace_bytes < need)
+        return Q4P_EWORKSPACE;
+    if (!workspace || !aligned(workspace, 4))
+        return Q4P_EINVAL;
+    if (overlap(workspace, need, w, wb) || overlap(workspace, need, codes, cb) ||
+        overlap(workspace, need, scales, sb) || overlap(workspace, need, global_scale, 4))
+        return Q4P_EINVAL;
+    q4proj_status st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_quantize(w, N, K, codes, scales, global_scale, workspace,
+                                           static_cast<hipStream_t>(stream)));
+}
+
 q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
                           float global_scale, const uint16_t *x, float *y, int64_t M, int64_t N,
                           int64_t K, void *workspace, size_t workspace_bytes, void *stream)

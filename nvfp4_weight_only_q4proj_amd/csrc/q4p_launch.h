@@ -41,4 +41,12 @@ hipError_t launch_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *pack
                                 float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
                                 int64_t K, hipStream_t stream);
 
+// NVFP4 quantizer: bf16 W [N][K] -> canonical codes, scales, global scale
+// (device float).  workspace: quant_workspace_bytes(), no initial contents.
+size_t quant_workspace_bytes();
+
+hipError_t launch_quantize(const uint16_t *w, int64_t N, int64_t K, uint8_t *codes,
+                           uint8_t *scales, float *global_scale, void *workspace,
+                           hipStream_t stream);
+
 }  // namespace q4p

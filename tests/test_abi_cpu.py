@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(q4):
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 14, names
     lib = q4.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -170,6 +170,25 @@ def test_silu_mul_validation(q4):
         assert silu(lib, **{"fn": "q4proj_gemm_silu_mul", "M": 512, **kw}) == q4.EINVAL, kw
 
 
+def test_quantize_validation(q4):
+    lib = q4.library()
+    assert q4.q4proj_quantize_workspace_bytes(16, 128) == 4096
+    assert q4.q4proj_quantize_workspace_bytes(16, 120) == 0
+    assert q4.q4proj_quantize_workspace_bytes(0, 128) == 0
+    C, S, G = X, Y, W + 65536
+
+    def quant(w=A, N=16, K=128, codes=C, scales=S, g=G, ws=W, wsb=4096):
+        return lib.q4proj_quantize(w, N, K, codes, scales, g, ws, wsb, None)
+
+    for kw in [dict(w=None), dict(codes=None), dict(scales=None), dict(g=None), dict(N=0),
+               dict(K=0), dict(K=24), dict(N=-1), dict(w=A + 8), dict(codes=C + 4), dict(g=G + 2),
+               dict(codes=A), dict(scales=A + 64), dict(scales=C + 16), dict(g=S), dict(ws=None),
+               dict(ws=W + 2), dict(ws=G - 16)]:
+        assert quant(**kw) == q4.EINVAL, kw
+    assert quant(wsb=4095) == q4.EWORKSPACE
+    assert quant(ws=None, wsb=0) == q4.EWORKSPACE
+
+
 @pytest.mark.parametrize("fn", ["q4proj_pack", "q4proj_unpack"])
 def test_pack_validation(q4, fn):
     lib = q4.library()
@@ -201,3 +220,4 @@ def test_no_device_no_fallback(q4):
     assert silu(lib) == q4.EDEVICE
     assert silu(lib, h=Y + 2) == q4.EDEVICE             # bf16 out needs 2-byte alignment only
     assert silu(lib, fn="q4proj_gemm_silu_mul", M=512, ws=None, wsb=0) == q4.EDEVICE
+    assert lib.q4proj_quantize(A, 16, 128, X, Y, W + 65536, W, 4096, None) == q4.EDEVICE
