@@ -11,6 +11,8 @@ with gcc into ``liboracle.so`` and exposes numpy-level wrappers:
 * :func:`dequant_row` — one weight row in fp64,
 * :func:`proj` / :func:`proj_rows` — y and the tolerance base S in fp64,
 * :func:`check` — the acceptance test |y_gpu - y_ref| <= rtol * S,
+* :func:`argmax_check` — the acceptance test of a greedy argmax (index and
+  value) over logits rows,
 * :func:`quantize` / :func:`quant_global_scale` — the NVFP4 quantizer
   (bf16 weights -> codes, e4m3 block scales, global scale), decisions in fp32,
 * :func:`silu_mul_cols` / :func:`check_bf16` — the fused gate/up projection
@@ -77,6 +79,8 @@ def load(path: str = LIB):
     lib.orc_silu_mul_bound.restype = None
     lib.orc_check_bf16.argtypes = [i64, vp, vp, vp, ctypes.POINTER(dbl)]
     lib.orc_check_bf16.restype = i64
+    lib.orc_argmax_check.argtypes = [i64, i64, vp, vp, dbl, vp, vp]
+    lib.orc_argmax_check.restype = i64
     lib.orc_quant_e4m3.argtypes = [ctypes.c_float]
     lib.orc_quant_e4m3.restype = ctypes.c_uint
     lib.orc_quant_e2m1.argtypes = [ctypes.c_float]
@@ -240,4 +244,16 @@ def quantize(w_bits, N: int, K: int, g=None, rows=None, lib=None):
     scales = np.empty((R, K // 16), dtype=np.uint8)
     lib.orc_quantize(R, K, _ptr(w), float(g), _ptr(codes), _ptr(scales))
     return codes, scales, float(g)
+
+
+def argmax_check(y_ref, S, idx, val, rtol: float = RTOL, lib=None) -> int:
+    """Rows whose (index, value) is not an acceptable greedy argmax of the
+    exact logits y_ref [M][N] (tolerance bases S); returns the count."""
+    yr = np.ascontiguousarray(y_ref, dtype=np.float64)
+    sr = np.ascontiguousarray(S, dtype=np.float64)
+    M, N = yr.shape
+    ix = np.ascontiguousarray(idx, dtype=np.int64).reshape(M)
+    vv = np.ascontiguousarray(val, dtype=np.float32).reshape(M)
+    return int((lib or load()).orc_argmax_check(M, N, _ptr(yr), _ptr(sr), float(rtol), _ptr(ix),
+                                                _ptr(vv)))
 

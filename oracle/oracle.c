@@ -446,3 +446,54 @@ void orc_quantize(int64_t N, int64_t K, const uint16_t *w, float g, uint8_t *cod
         }
     }
 }
+
+/* ---- greedy argmax of a logits row --------------------------------------
+ *
+ * The FlashRT "Qwen3.6 NVFP4 usage" page decodes greedily: each next token is
+ * the argmax of the logits row (per-step forward example; the speculative
+ * path is greedy-only).  The GPU decides on its fp32 logits, which may order
+ * two logits differently from the exact values when they lie within the
+ * projection tolerance of each other, so several indices can be correct.
+ * For row m with exact logits yref and tolerance bases S (orc_proj):
+ *   - a row holding a NaN must return its first NaN column, with a NaN value
+ *     (NaN positions are exact: they come from NaN block scales);
+ *   - otherwise index i is accepted when yref[i] + rtol*S[i] >= max over j of
+ *     (yref[j] - rtol*S[j])  (i can be the largest within tolerance), and the
+ *     returned value v when |v - yref[i]| <= rtol*S[i].
+ * Returns the number of rejected rows.
+ */
+int64_t orc_argmax_check(int64_t M, int64_t N, const double *yref, const double *S,
+                         double rtol, const int64_t *idx, const float *val)
+{
+    int64_t bad = 0;
+    for (int64_t m = 0; m < M; ++m) {
+        const double *yr = yref + m * N, *sr = S + m * N;
+        const int64_t i = idx[m];
+        const double v = (double)val[m];
+        int64_t first_nan = -1;
+        double floor_max = -INFINITY;
+        for (int64_t j = 0; j < N; ++j) {
+            if (isnan(yr[j])) {
+                if (first_nan < 0)
+                    first_nan = j;
+                continue;
+            }
+            const double lo = yr[j] - rtol * sr[j];
+            if (lo > floor_max)
+                floor_max = lo;
+        }
+        if (i < 0 || i >= N) {
+            ++bad;
+            continue;
+        }
+        if (first_nan >= 0) {
+            if (i != first_nan || !isnan(v))
+                ++bad;
+            continue;
+        }
+        const double tol = rtol * sr[i];
+        if (!(yr[i] + tol >= floor_max) || !(fabs(v - yr[i]) <= tol))
+            ++bad;
+    }
+    return bad;
+}

@@ -385,6 +385,43 @@ def pin_silu_mul_bound(lib):
         assert bad == 1, (i, v, bad)
 
 
+# ---- greedy argmax acceptance ----------------------------------------------
+
+def pin_argmax_check(lib):
+    """The argmax acceptance test: with a clear maximum only torch.argmax's
+    index (and a value within tolerance of it) passes; two logits within
+    tolerance of each other both pass, one clearly below does not; a row
+    with NaNs accepts only its first NaN column with a NaN value; indices out
+    of range fail."""
+    rng = np.random.default_rng(13)
+    M, N = 3, 50
+    y = rng.normal(0, 1, (M, N))
+    S = np.full((M, N), 1.0)
+    rt = 1e-3                                        # tolerance 1e-3 per element
+    y[0, 17] = 10.0                                  # clear maximum
+    y[1, 3], y[1, 40] = 5.0, 5.0015                  # within 2e-3 of each other
+    y[1, 41] = 4.99                                  # clearly below
+    y[2, 9] = np.nan
+    y[2, 30] = np.nan
+    want0 = int(torch.argmax(torch.from_numpy(y[0])))
+    assert want0 == 17
+
+    def run(rows_idx, rows_val):
+        return oracle.argmax_check(y, S, np.array(rows_idx), np.array(rows_val, np.float32),
+                                   rtol=rt, lib=lib)
+
+    base_i, base_v = [17, 40, 9], [10.0, 5.0015, np.nan]
+    assert run(base_i, base_v) == 0
+    assert run([3, 3, 9], [10.0, 5.0, np.nan]) == 1          # row 0: not the maximum
+    assert run([17, 3, 9], [10.0, 5.0, np.nan]) == 0         # row 1: within tolerance
+    assert run([17, 41, 9], [10.0, 4.99, np.nan]) == 1       # row 1: clearly below
+    assert run([17, 40, 30], [10.0, 5.0015, np.nan]) == 1    # row 2: not the first NaN
+    assert run([17, 40, 9], [10.0, 5.0015, 1.0]) == 1        # row 2: value not NaN
+    assert run([17, 40, 9], [10.002, 5.0015, np.nan]) == 1   # row 0: value off
+    assert run([-1, 40, 9], [10.0, 5.0015, np.nan]) == 1
+    assert run([17, N, 9], [10.0, 5.0015, np.nan]) == 1
+
+
 # ---- the NVFP4 quantizer ----------------------------------------------------
 
 def golden_e2m1_rounding():
@@ -522,4 +559,4 @@ ALL_PINS = [pin_e2m1_table, pin_e4m3_torch, pin_e4m3_landmarks, pin_bf16_torch,
             pin_invariants, pin_nan_scale, pin_check, pin_silu_mul_torch,
             pin_silu_mul_fused_rows, pin_silu_mul_bound, pin_quant_e2m1_rounding,
             pin_quant_e4m3_torch, pin_quant_global_scale, pin_quantize_exact_recovery,
-            pin_quantize_nearest]
+            pin_quantize_nearest, pin_argmax_check]

@@ -62,6 +62,10 @@ MUTANTS = {
     "quant_sign_dropped": ("quant_e2m1(r) | ((bits >> 15) << 3)", "quant_e2m1(r)", 1),
     "quant_unit_without_g": ("(float)orc_e4m3(s) * g;", "(float)orc_e4m3(s);", 1),
     "quant_nibbles_swapped": ("(uint8_t)(q[0] | (q[1] << 4))", "(uint8_t)(q[1] | (q[0] << 4))", 1),
+    "argmax_no_tolerance": ("if (!(yr[i] + tol >= floor_max)", "if (!(yr[i] >= floor_max + tol)", 1),
+    "argmax_any_nan": ("if (i != first_nan || !isnan(v))", "if (!isnan(yr[i]) || !isnan(v))", 1),
+    "argmax_value_unchecked": ("|| !(fabs(v - yr[i]) <= tol))", ")", 1),
+    "argmax_upper_floor": ("const double lo = yr[j] - rtol * sr[j];", "const double lo = yr[j] + rtol * sr[j];", 1),
     "quant_block_amax_first": ("if (a > amax_b)\n                    amax_b = a;", "if (i == 0)\n                    amax_b = a;", 1),
 }
 
