@@ -26,6 +26,9 @@ Also measured and reported in the same JSON line:
                 each beside the plain projection over the same packed weight
                 (fp32 out, no epilogue).
   pack          the one-time weight swizzle (read + write bytes / s).
+  lm_head_argmax  the lm-head GEMV (M = 1 decode, M = 7 verify) with the fused
+                greedy argmax and no logits written, beside the plain GEMV
+                writing the logits followed by torch.argmax.
   quantize      the load-time NVFP4 conversion of bf16 weights (fused gate/up
                 34816 x 5120 and lm-head 248320 x 5120): algorithmic bytes
                 (bf16 in, codes + scales out) / s; two launches, the first
@@ -113,7 +116,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="wall-time bound of the cpu_baseline sample")
-    ap.add_argument("--only", choices=["dec", "pre", "mlp", "quant", "all"], default="all",
+    ap.add_argument("--only", choices=["dec", "pre", "mlp", "argmax", "quant", "all"],
+                    default="all",
                     help="restrict the run (for profiling one kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run a plain 256 MiB device copy (counter calibration)")
@@ -338,6 +342,46 @@ def main():
             "per_M": fused,
             "kernel_source_sha256_16": {"gemv": src_digest("q4p_gemv.hip"),
                                         "gemm": src_digest("q4p_gemm.hip")}}
+
+    # ---- lm-head with the fused greedy argmax ------------------------------
+    if args.only in ("argmax", "all"):
+        (c,) = synth.workload_cases("lmh", only=["lm_head"])
+        N, K = c.N, c.K
+        lm = {}
+        for M in (1, 7):
+            cm = synth.Case("lmh", c.name, M, c.matrix,
+                            c.x if M == 1 else synth.x_bf16(4, 20 + M, M, K))
+            u = upload(cm, copies_for(algo_bytes(M, N, K)))
+            val = torch.empty(M, dtype=torch.float32, device=dev)
+            idx = torch.empty(M, dtype=torch.int64, device=dev)
+            ws = torch.zeros(q4.q4proj_argmax_workspace_bytes(M, N, K), dtype=torch.uint8,
+                             device=dev)
+
+            def fused(i, u=u, val=val, idx=idx, ws=ws, M=M):
+                pc, ps = u["w"][i % len(u["w"])]
+                return lambda: q4.q4proj_gemv_argmax(pc, ps, u["g"], u["x"], None, val, idx,
+                                                     M, N, K, workspace=ws)
+
+            def unfused(i, u=u):
+                f = launcher("gemv", u, i)
+                return lambda: (f(), torch.argmax(u["y"], dim=1))
+
+            n = max(10, args.steps // 8)
+            for i in range(3):
+                fused(i)()
+                unfused(i)()
+            ms_f, _ = timed_region(torch, [fused(i) for i in range(n)], n)
+            ms_u, _ = timed_region(torch, [unfused(i) for i in range(n)], n)
+            b = N * K // 2 + N * K // 16 + 2 * M * K + 12 * M + 4
+            lm[f"M={M}"] = {"M": M, "N": N, "K": K, "us": round(ms_f * 1e3, 2),
+                            "gbs": round(b / (ms_f * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(b / (ms_f * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "gemv_plus_torch_argmax_us": round(ms_u * 1e3, 2)}
+            del u, val, idx, ws
+        out["lm_head_argmax"] = {
+            "workload": "lm-head 5120 -> 248320 NVFP4 GEMV + greedy argmax, no logits written",
+            "kernel": "gemv_sk_kernel<ROWS, 4, false, 2>", "per_M": lm,
+            "kernel_source_sha256_16": src_digest("q4p_gemv.hip")}
 
     # ---- NVFP4 quantizer --------------------------------------------------
     if args.only in ("quant", "all"):

@@ -205,6 +205,43 @@ q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                    size_t workspace_bytes, void *stream);
 
 /*
+ * Device scratch q4proj_gemv_argmax needs for (M, N, K): the q4proj_gemv
+ * workspace of the same shape plus 8 * (M + 1) bytes (one 64-bit key per row
+ * and a completion counter); 0 when the entry point does not serve the shape
+ * (as q4proj_gemv_silu_mul: M outside 1..16, invalid N/K, or K past the
+ * eight-range limit).  Zero-filled by the caller before first use, left
+ * zero-filled by every completed call; one per stream.
+ */
+size_t q4proj_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
+ * q4proj_gemv_argmax — the lm-head GEMV with a fused greedy argmax,
+ * 1 <= M <= 16.  The FlashRT "Qwen3.6 NVFP4 usage" page decodes greedily
+ * only (speculative-decode section: the public path is greedy, a
+ * deterministic argmax sequence) and picks each token as the argmax of the
+ * logits row (its per-step forward example); verify takes the argmax of each
+ * of its K+1 rows.
+ *     logits[m][n] = y[m][n] as q4proj_gemv computes it (fp32)
+ *     max_idx[m]   = the first n with the largest logits[m][n]; NaN counts
+ *                    as larger than every number and -0 equals +0
+ *     max_val[m]   = logits[m][max_idx[m]]   (bit for bit, a NaN as the
+ *                    canonical quiet NaN)
+ * y may be NULL: then the logits are not written at all.  The decision is
+ * taken on the fp32 logits the kernel computes; deterministic.
+ *     max_val float [M], max_idx int64 [M]: device memory, 4- and 8-byte
+ *     aligned.
+ * Errors: EINVAL (null pointer other than y, M/N/K <= 0, K % 16 != 0,
+ *         misalignment, outputs overlapping inputs or each other, workspace
+ *         overlapping any argument), EUNSUPPORTED (M > 16, or K too long),
+ *         EWORKSPACE, EDEVICE, EHIP.
+ */
+q4proj_status q4proj_gemv_argmax(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                 float global_scale, const uint16_t *x, float *y,
+                                 float *max_val, int64_t *max_idx, int64_t M, int64_t N,
+                                 int64_t K, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
  * Device scratch q4proj_quantize needs: 4096 bytes for every valid (N, K),
  * 0 otherwise.  No initial contents are required and none are kept between
  * calls; calls that may run at the same time need separate workspaces.

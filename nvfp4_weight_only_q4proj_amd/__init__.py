@@ -52,6 +52,11 @@ _lib.q4proj_gemv_silu_mul.argtypes = _PROJ_ARGS
 _lib.q4proj_gemv_silu_mul.restype = ctypes.c_int
 _lib.q4proj_gemm_silu_mul.argtypes = _PROJ_ARGS
 _lib.q4proj_gemm_silu_mul.restype = ctypes.c_int
+_lib.q4proj_argmax_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.q4proj_argmax_workspace_bytes.restype = _sz
+_lib.q4proj_gemv_argmax.argtypes = [_vp, _vp, _f32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz,
+                                    _vp]
+_lib.q4proj_gemv_argmax.restype = ctypes.c_int
 _lib.q4proj_quantize_workspace_bytes.argtypes = [_i64, _i64]
 _lib.q4proj_quantize_workspace_bytes.restype = _sz
 _lib.q4proj_quantize.argtypes = [_vp, _i64, _i64, _vp, _vp, _vp, _vp, _sz, _vp]
@@ -65,6 +70,7 @@ _lib.q4proj_last_hip_error.restype = ctypes.c_char_p
 SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
            "q4proj_pack", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
            "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul", "q4proj_gemm_silu_mul",
+           "q4proj_argmax_workspace_bytes", "q4proj_gemv_argmax",
            "q4proj_quantize_workspace_bytes", "q4proj_quantize",
            "q4proj_status_string", "q4proj_last_hip_error")
 
@@ -248,6 +254,37 @@ def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, 
         _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
                   x.data_ptr(), h.data_ptr(), M, F, K, ws_ptr, ws_bytes, _stream(x, stream)),
                where)
+
+
+def q4proj_argmax_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.q4proj_argmax_workspace_bytes(M, N, K))
+
+
+def q4proj_gemv_argmax(packed_codes, packed_scales, global_scale: float, x, y, max_val, max_idx,
+                       M: int, N: int, K: int, workspace=None, stream=None) -> None:
+    """Greedy argmax of each row of the logits x . dequant(W)^T (1 <= M <= 16):
+    max_val float32 [M], max_idx int64 [M]; y (fp32 [M][N]) may be None."""
+    dev = x.device
+    _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
+    _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
+    x = _bf16_bits(x, "x")
+    _need(x, "x", x.dtype, M * K, dev)
+    if y is not None:
+        _need(y, "y", torch.float32, M * N, dev)
+    _need(max_val, "max_val", torch.float32, M, dev)
+    _need(max_idx, "max_idx", torch.int64, M, dev)
+    if workspace is None:
+        workspace = default_workspace(dev, q4proj_argmax_workspace_bytes(M, N, K))
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
+        ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    with torch.cuda.device(dev):
+        _check(_lib.q4proj_gemv_argmax(packed_codes.data_ptr(), packed_scales.data_ptr(),
+                                       float(global_scale), x.data_ptr(),
+                                       None if y is None else y.data_ptr(), max_val.data_ptr(),
+                                       max_idx.data_ptr(), M, N, K, ws_ptr, ws_bytes,
+                                       _stream(x, stream)), "q4proj_gemv_argmax")
 
 
 def q4proj_quantize_workspace_bytes(N: int, K: int) -> int:

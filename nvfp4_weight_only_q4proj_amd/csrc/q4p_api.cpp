@@ -254,6 +254,66 @@ q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                                 M, F, K, static_cast<hipStream_t>(stream)));
 }
 
+size_t q4proj_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || M > Q4PROJ_GEMV_MAX_M || !shape_ok(N, K))
+        return 0;
+    return q4p::gemv_argmax_workspace_bytes(M, N, K);
+}
+
+q4proj_status q4proj_gemv_argmax(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                 float global_scale, const uint16_t *x, float *y,
+                                 float *max_val, int64_t *max_idx, int64_t M, int64_t N,
+                                 int64_t K, void *workspace, size_t workspace_bytes,
+                                 void *stream)
+{
+    if (!packed_codes || !packed_scales || !x || !max_val || !max_idx)
+        return Q4P_EINVAL;
+    if (M <= 0 || M > (int64_t)1 << 24 || !shape_ok(N, K))
+        return Q4P_EINVAL;
+    if ((uint64_t)M * (uint64_t)N > ((uint64_t)1 << 40))
+        return Q4P_EINVAL;
+    if (!aligned(packed_codes, 16) || !aligned(packed_scales, 8) || !aligned(x, 16) ||
+        (y && !aligned(y, 4)) || !aligned(max_val, 4) || !aligned(max_idx, 8))
+        return Q4P_EINVAL;
+    const size_t xb = (size_t)M * (size_t)K * 2, yb = (size_t)M * (size_t)N * 4;
+    const size_t vb = (size_t)M * 4, ib = (size_t)M * 8;
+    const size_t pcb = q4proj_packed_codes_bytes(N, K), psb = q4proj_packed_scales_bytes(N, K);
+    const void *outs[3] = {y, max_val, max_idx};
+    const size_t outb[3] = {yb, vb, ib};
+    for (int i = 0; i < 3; ++i) {
+        if (!outs[i])
+            continue;
+        if (overlap(outs[i], outb[i], x, xb) || overlap(outs[i], outb[i], packed_codes, pcb) ||
+            overlap(outs[i], outb[i], packed_scales, psb))
+            return Q4P_EINVAL;
+        for (int j = i + 1; j < 3; ++j)
+            if (outs[j] && overlap(outs[i], outb[i], outs[j], outb[j]))
+                return Q4P_EINVAL;
+    }
+    if (M > Q4PROJ_GEMV_MAX_M)
+        return Q4P_EUNSUPPORTED;
+    const size_t need = q4proj_argmax_workspace_bytes(M, N, K);
+    if (need == 0)
+        return Q4P_EUNSUPPORTED;
+    if (workspace_bytes < need)
+        return Q4P_EWORKSPACE;
+    if (!workspace || !aligned(workspace, 8))
+        return Q4P_EINVAL;
+    if (overlap(workspace, need, x, xb) || overlap(workspace, need, packed_codes, pcb) ||
+        overlap(workspace, need, packed_scales, psb))
+        return Q4P_EINVAL;
+    for (int i = 0; i < 3; ++i)
+        if (outs[i] && overlap(workspace, need, outs[i], outb[i]))
+            return Q4P_EINVAL;
+    q4proj_status st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_gemv_argmax(packed_codes, packed_scales, global_scale, x, y,
+                                              max_val, max_idx, M, N, K, workspace,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 size_t q4proj_quantize_workspace_bytes(int64_t N, int64_t K)
 {
     return shape_ok(N, K) ? q4p::quant_workspace_bytes() : 0;

@@ -404,7 +404,40 @@ struct SkArgs {
     int M, N, K, KT, NT, G, WPG;
     int KS, KTR;                               // K ranges, k-tiles per range (last may be shorter)
     float g;
+    float *best_val;                           // argmax epilogue: per-row result
+    int64_t *best_idx;
 };
+
+// Epilogues of the stream-K kernel
+constexpr int kEpiY = 0;                       // y = g * acc (fp32)
+constexpr int kEpiSilu = 1;                    // fused gate/up: h = bf16(silu(gate) * up)
+constexpr int kEpiArgmax = 2;                  // y optional; per-row max value and index
+
+// Argmax key of value v at column col: an order-preserving map of v in the
+// high half (NaN above every number, -0 equal to +0) and ~col in the low half,
+// so the largest key is the largest value at its lowest column -- the first
+// maximum, NaN counting as the largest, as a greedy argmax over the logits
+// reads it.  Max over keys is exact and order-independent.
+__device__ __forceinline__ unsigned long long argmax_key(float v, int col)
+{
+    const uint32_t b = __builtin_bit_cast(uint32_t, v);
+    uint32_t o;
+    if ((b & 0x7FFFFFFFu) > 0x7F800000u)
+        o = 0xFFFFFFFFu;
+    else if ((b & 0x7FFFFFFFu) == 0u)
+        o = 0x80000000u;
+    else
+        o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((unsigned long long)o << 32) | (0xFFFFFFFFu - (uint32_t)col);
+}
+
+__device__ __forceinline__ float argmax_key_value(unsigned long long k)
+{
+    const uint32_t o = (uint32_t)(k >> 32);
+    if (o == 0xFFFFFFFFu)
+        return __builtin_nanf("");
+    return __builtin_bit_cast(float, (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o);
+}
 
 // A gate/up pair of partial sums in one 64-bit exchange word.  Both fields
 // are XORed with a NaN pattern that no stored value has (a NaN is stored as
@@ -440,12 +473,27 @@ __device__ __forceinline__ float pair_up(unsigned long long w)
 // to lane r; exchanges between workgroups and K ranges then carry (gate, up)
 // in one word from lane r, and the side that completes a pair applies the
 // epilogue.  out is bf16 h[M][F] instead of fp32 y[M][N].
-template <int ROWS, int PF, bool KR, bool SILU>
+//
+// ARGMAX: y is stored only when out is not null; every completed output also
+// updates its lane's running best key per row (argmax_key).  After the finish
+// the workgroup reduces its keys (16 lanes, then the waves through LDS) and
+// adds them to one 64-bit atomic max per row in the workspace, waits for
+// those atomics to return, and counts itself done on a counter word; the
+// workgroup that brings the count to G reads and clears the row keys with
+// atomic exchanges, clears the counter and writes each row's value and
+// index.  The row keys and the counter are touched only by device-scope
+// atomics, which are performed where all XCDs see them, and an atomic that
+// has returned has been performed: so no cache write-back or invalidation
+// is needed (an agent-scope fence here costs an L2 write-back per workgroup
+// while others are still streaming).
+template <int ROWS, int PF, bool KR, int EPI>
 __global__ void __launch_bounds__(64 * kSkMaxWaves)
 gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
                const uint16_t *__restrict__ x, void *__restrict__ out,
                unsigned long long *__restrict__ xch, SkArgs a)
 {
+    constexpr bool SILU = EPI == kEpiSilu;
+    constexpr bool ARGMAX = EPI == kEpiArgmax;
     extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int lane = threadIdx.x & 63;
@@ -597,7 +645,8 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     // the other ranges' values along the tree -- at each level the side that
     // finds its partner's value adds the two, clears the word and goes on --
     // and stored by the last join (at once when there is one range).
-    auto join = [&](int m, int col, float v) {
+    unsigned long long bestk[4] = {0ull, 0ull, 0ull, 0ull};   // ARGMAX: per row slot j
+    auto join = [&](int m, int col, float v, int j) {
         for (int span = 1; span < (KR ? a.KS : 1); span *= 2) {
             const int set = (a.KS - a.KS / span) + kr / (2 * span);
             unsigned long long *wd = xch + kSkBoundaryWords + ((int64_t)set * M + m) * N + col;
@@ -610,7 +659,13 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             v = __builtin_bit_cast(float, (uint32_t)old) + v;
             __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
-        y[(int64_t)m * N + col] = g * v;
+        const float gv = g * v;
+        if (!ARGMAX || y != nullptr)
+            y[(int64_t)m * N + col] = gv;
+        if (ARGMAX) {
+            const unsigned long long k = argmax_key(gv, col);
+            bestk[j] = k > bestk[j] ? k : bestk[j];
+        }
     };
     // SILU: the same for this range's complete gate and up values of output
     // (m, f), one word per pair; the last join applies the epilogue
@@ -653,7 +708,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                 const int m = 4 * gq + j;
                 const float vj = v[j];
                 if (m < M)
-                    join(m, col, vj);
+                    join(m, col, vj, j);
             }
         }
     };
@@ -706,10 +761,8 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
 
     // 5. finish the row tiles split between waves or workgroups
     __syncthreads();
-    if (n == 0)
-        return;
-    const int tlast = (u1 - 1) / KT;
-    for (int side = 0; side < 2; ++side) {
+    const int tlast = n > 0 ? (u1 - 1) / KT : 0;
+    for (int side = 0; side < (n > 0 ? 2 : 0); ++side) {
         const int tau = side == 0 ? tfirst : tlast;
         if (side == 1 && tlast == tfirst)
             break;
@@ -769,9 +822,56 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                     const float other = __builtin_bit_cast(float, (uint32_t)old);
                     __hip_atomic_store(slot + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
                     if (col < N)
-                        join(m, col, other + sj);
+                        join(m, col, other + sj, j);
                 }
             }
+        }
+    }
+
+    if (ARGMAX) {
+        // part[] is free once every wave is past the finish
+        unsigned long long *red = reinterpret_cast<unsigned long long *>(part);
+        unsigned long long *keys = xch + kSkBoundaryWords + (int64_t)(a.KS - 1) * M * N;
+        unsigned long long *counter = keys + M;
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < ROWS; ++j) {
+            unsigned long long k = bestk[j];
+#pragma unroll
+            for (int off = 1; off < 16; off <<= 1) {
+                const unsigned long long o = __shfl_xor(k, off, 64);
+                k = o > k ? o : k;
+            }
+            if (r == 0)
+                red[wave * 16 + 4 * gq + j] = k;
+        }
+        __syncthreads();
+        if ((int)threadIdx.x < M) {
+            unsigned long long k = red[threadIdx.x];
+            for (int v = 1; v < WPG; ++v) {
+                const unsigned long long o = red[v * 16 + threadIdx.x];
+                k = o > k ? o : k;
+            }
+            const unsigned long long prev = __hip_atomic_fetch_max(
+                keys + threadIdx.x, k, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            asm volatile("" ::"v"(prev) : "memory");       // the max has returned
+        }
+        __syncthreads();
+        if (threadIdx.x == 0) {
+            const unsigned long long done = __hip_atomic_fetch_add(
+                counter, 1ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            red[0] = done == (unsigned long long)(G - 1) ? 1ull : 0ull;
+        }
+        __syncthreads();
+        if (red[0] != 0ull) {
+            if ((int)threadIdx.x < M) {
+                const unsigned long long k = __hip_atomic_exchange(
+                    keys + threadIdx.x, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                a.best_val[threadIdx.x] = argmax_key_value(k);
+                a.best_idx[threadIdx.x] = (int64_t)(0xFFFFFFFFu - (uint32_t)k);
+            }
+            if (threadIdx.x == 0)
+                __hip_atomic_store(counter, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         }
     }
 }
@@ -887,22 +987,30 @@ Plan cached_plan(int64_t M, int64_t N, int64_t K)
 typedef void (*gemv_sk_fn)(const uint4 *, const uint2 *, const uint16_t *, void *,
                            unsigned long long *, SkArgs);
 
-template <bool KR, bool SILU>
+template <bool KR, int EPI>
 gemv_sk_fn pick_sk_kernel_k(int64_t M)
 {
     switch (M) {
-    case 1: return gemv_sk_kernel<1, kSkPrefetch, KR, SILU>;
-    case 2: return gemv_sk_kernel<2, kSkPrefetch, KR, SILU>;
-    case 3: return gemv_sk_kernel<3, kSkPrefetch, KR, SILU>;
-    default: return gemv_sk_kernel<4, kSkPrefetch, KR, SILU>;
+    case 1: return gemv_sk_kernel<1, kSkPrefetch, KR, EPI>;
+    case 2: return gemv_sk_kernel<2, kSkPrefetch, KR, EPI>;
+    case 3: return gemv_sk_kernel<3, kSkPrefetch, KR, EPI>;
+    default: return gemv_sk_kernel<4, kSkPrefetch, KR, EPI>;
     }
 }
 
-gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges, bool silu)
+template <int EPI>
+gemv_sk_fn pick_sk_kernel_e(int64_t M, bool ranges)
 {
-    if (silu)
-        return ranges ? pick_sk_kernel_k<true, true>(M) : pick_sk_kernel_k<false, true>(M);
-    return ranges ? pick_sk_kernel_k<true, false>(M) : pick_sk_kernel_k<false, false>(M);
+    return ranges ? pick_sk_kernel_k<true, EPI>(M) : pick_sk_kernel_k<false, EPI>(M);
+}
+
+gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges, int epi)
+{
+    switch (epi) {
+    case kEpiSilu: return pick_sk_kernel_e<kEpiSilu>(M, ranges);
+    case kEpiArgmax: return pick_sk_kernel_e<kEpiArgmax>(M, ranges);
+    default: return pick_sk_kernel_e<kEpiY>(M, ranges);
+    }
 }
 
 // K ranges for the stream-K kernel: the fewest (a power of two) whose
@@ -934,7 +1042,7 @@ struct SkPlan {
 // One workgroup per CU (at most kSkMaxGroups), but no more workgroups than
 // row tiles, so that every workgroup's range covers at least KT units and a
 // row tile is shared by at most two workgroups.
-SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
+SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, int epi)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
     const int64_t KS = sk_ranges(M, K);
@@ -951,9 +1059,9 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
     if (WPG > ULAST / GR)
         WPG = ULAST / GR;
     SkPlan p;
-    p.fn = pick_sk_kernel(M, KS > 1, silu);
+    p.fn = pick_sk_kernel(M, KS > 1, epi);
     p.args = SkArgs{(int)M, (int)N, (int)K, (int)KT, (int)NT, (int)(GR * KS), (int)WPG, (int)KS,
-                    (int)KTR, 0.f};
+                    (int)KTR, 0.f, nullptr, nullptr};
     size_t lds = (size_t)(M * KTR * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
     if (lds < (size_t)kSkLdsFloor)
         lds = kSkLdsFloor;
@@ -964,11 +1072,11 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
 struct CachedSkPlan {
     int dev;
     int64_t M, N, K;
-    bool silu;
+    int epi;
     SkPlan plan;
 };
 
-SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
+SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K, int epi)
 {
     static std::mutex mu;
     static std::vector<CachedSkPlan> cache;
@@ -976,12 +1084,12 @@ SkPlan cached_sk_plan(int64_t M, int64_t N, int64_t K, bool silu)
     (void)hipGetDevice(&dev);
     std::lock_guard<std::mutex> lock(mu);
     for (const CachedSkPlan &c : cache)
-        if (c.dev == dev && c.M == M && c.N == N && c.K == K && c.silu == silu)
+        if (c.dev == dev && c.M == M && c.N == N && c.K == K && c.epi == epi)
             return c.plan;
-    const SkPlan p = make_sk_plan(M, N, K, silu);
+    const SkPlan p = make_sk_plan(M, N, K, epi);
     if (cache.size() >= 256)
         cache.clear();
-    cache.push_back({dev, M, N, K, silu, p});
+    cache.push_back({dev, M, N, K, epi, p});
     return p;
 }
 
@@ -1014,7 +1122,7 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
     if (sk_usable(M, N, K)) {
-        const SkPlan p = cached_sk_plan(M, N, K, false);
+        const SkPlan p = cached_sk_plan(M, N, K, kEpiY);
         SkArgs args = p.args;
         args.g = g;
         hipLaunchKernelGGL(p.fn, dim3((unsigned)args.G), dim3(64 * args.WPG), p.lds, stream,
@@ -1037,12 +1145,44 @@ hipError_t launch_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *pack
 {
     if (!gemv_silu_mul_supported(M, F, K))
         return hipErrorInvalidValue;
-    const SkPlan p = cached_sk_plan(M, 2 * F, K, true);
+    const SkPlan p = cached_sk_plan(M, 2 * F, K, kEpiSilu);
     SkArgs args = p.args;
     args.g = g;
     hipLaunchKernelGGL(p.fn, dim3((unsigned)args.G), dim3(64 * args.WPG), p.lds, stream,
                        reinterpret_cast<const uint4 *>(packed_codes),
                        reinterpret_cast<const uint2 *>(packed_scales), x, h,
+                       static_cast<unsigned long long *>(workspace), args);
+    return hipGetLastError();
+}
+
+bool gemv_argmax_supported(int64_t M, int64_t N, int64_t K)
+{
+    return M >= 1 && M <= 16 && N >= 1 && K >= 1 && sk_usable(M, N, K);
+}
+
+size_t gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (!gemv_argmax_supported(M, N, K))
+        return 0;
+    // the GEMV's exchange words, then one key per row and the counter
+    return gemv_workspace_bytes(M, N, K) + (size_t)(M + 1) * sizeof(unsigned long long);
+}
+
+hipError_t launch_gemv_argmax(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
+                              const uint16_t *x, float *y, float *best_val, int64_t *best_idx,
+                              int64_t M, int64_t N, int64_t K, void *workspace,
+                              hipStream_t stream)
+{
+    if (!gemv_argmax_supported(M, N, K))
+        return hipErrorInvalidValue;
+    const SkPlan p = cached_sk_plan(M, N, K, kEpiArgmax);
+    SkArgs args = p.args;
+    args.g = g;
+    args.best_val = best_val;
+    args.best_idx = best_idx;
+    hipLaunchKernelGGL(p.fn, dim3((unsigned)args.G), dim3(64 * args.WPG), p.lds, stream,
+                       reinterpret_cast<const uint4 *>(packed_codes),
+                       reinterpret_cast<const uint2 *>(packed_scales), x, y,
                        static_cast<unsigned long long *>(workspace), args);
     return hipGetLastError();
 }

@@ -32,6 +32,17 @@ hipError_t launch_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *pack
                                 float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
                                 int64_t K, void *workspace, hipStream_t stream);
 
+// Projection with a fused greedy-argmax epilogue (1 <= M <= 16, the shapes
+// the stream-K GEMV serves); y may be null.  Workspace: zero-filled before
+// first use, left zero-filled.
+bool gemv_argmax_supported(int64_t M, int64_t N, int64_t K);
+size_t gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+hipError_t launch_gemv_argmax(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
+                              const uint16_t *x, float *y, float *best_val, int64_t *best_idx,
+                              int64_t M, int64_t N, int64_t K, void *workspace,
+                              hipStream_t stream);
+
 hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(q4):
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 16, names
     lib = q4.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -170,6 +170,30 @@ def test_silu_mul_validation(q4):
         assert silu(lib, **{"fn": "q4proj_gemm_silu_mul", "M": 512, **kw}) == q4.EINVAL, kw
 
 
+def test_argmax_validation(q4):
+    lib = q4.library()
+    need = q4.q4proj_argmax_workspace_bytes(1, 64, 256)
+    assert need == 512 * 1024 + 16
+    assert q4.q4proj_argmax_workspace_bytes(17, 64, 256) == 0
+    assert q4.q4proj_argmax_workspace_bytes(16, 64, 32768 + 128) == 0
+    assert q4.q4proj_argmax_workspace_bytes(7, 5120, 17408) == 512 * 1024 + 8 * 7 * 5120 + 64
+    V, I = W + (1 << 20), W + (1 << 20) + 4096
+
+    def am(pc=A, ps=B, x=X, y=Y, val=V, idx=I, M=1, N=64, K=256, ws=W, wsb=need):
+        return lib.q4proj_gemv_argmax(pc, ps, ctypes.c_float(1.0), x, y, val, idx, M, N, K, ws,
+                                      wsb, None)
+
+    for kw in [dict(pc=None), dict(ps=None), dict(x=None), dict(val=None), dict(idx=None),
+               dict(M=0), dict(N=0), dict(K=24), dict(x=X + 8), dict(y=Y + 2), dict(val=V + 2),
+               dict(idx=I + 4), dict(y=X + 64), dict(val=A), dict(idx=V), dict(val=Y + 64),
+               dict(ws=None), dict(ws=W + 4), dict(ws=X), dict(ws=V - 64)]:
+        assert am(**kw) == q4.EINVAL, kw
+    assert am(M=17) == q4.EUNSUPPORTED
+    assert am(M=16, K=32768 + 128) == q4.EUNSUPPORTED
+    assert am(wsb=need - 8) == q4.EWORKSPACE
+    assert am(ws=None, wsb=0) == q4.EWORKSPACE
+
+
 def test_quantize_validation(q4):
     lib = q4.library()
     assert q4.q4proj_quantize_workspace_bytes(16, 128) == 4096
@@ -221,3 +245,6 @@ def test_no_device_no_fallback(q4):
     assert silu(lib, h=Y + 2) == q4.EDEVICE             # bf16 out needs 2-byte alignment only
     assert silu(lib, fn="q4proj_gemm_silu_mul", M=512, ws=None, wsb=0) == q4.EDEVICE
     assert lib.q4proj_quantize(A, 16, 128, X, Y, W + 65536, W, 4096, None) == q4.EDEVICE
+    assert lib.q4proj_gemv_argmax(A, B, ctypes.c_float(1.0), X, None, W + (1 << 20),
+                                  W + (1 << 20) + 4096, 1, 64, 256, W, 512 * 1024 + 16,
+                                  None) == q4.EDEVICE
