@@ -116,7 +116,7 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="wall-time bound of the cpu_baseline sample")
-    ap.add_argument("--only", choices=["dec", "pre", "mlp", "argmax", "quant", "all"],
+    ap.add_argument("--only", choices=["dec", "pre", "shapes", "mlp", "argmax", "quant", "all"],
                     default="all",
                     help="restrict the run (for profiling one kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -248,7 +248,7 @@ def main():
         del pre_u
 
     # ---- the other decode-type shapes, the pack step ------------------------
-    if args.only == "all":
+    if args.only in ("shapes", "all"):
         shapes = {}
         for wl in ("mtp", "lmh"):
             for c in synth.workload_cases(wl):
