@@ -199,7 +199,7 @@ def main():
                            u["w"][0][0].numel() + u["w"][0][1].numel() for u in dec_u)},
             "tokens_per_s": round(1.0 / (step_ms * 1e-3), 1),
             "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-            "roofline": {"bound": "hbm", "kernel": "gemv_sk_kernel<1, 4, false, false>",
+            "roofline": {"bound": "hbm", "kernel": "gemv_sk_kernel<1, 4, false, 0>",
                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "mean_launch_us": round(gemv_ms * 1e3, 3),
