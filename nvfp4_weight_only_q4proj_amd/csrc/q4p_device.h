@@ -36,6 +36,7 @@ typedef short short4_t __attribute__((ext_vector_type(4)));
 typedef float floatx2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 
 // 16-byte load of data that is read exactly once (packed weights): marked
 // non-temporal so it does not displace the activations from the caches.

@@ -565,20 +565,33 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             xs[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)srow[i] * K + k);
     }
 
-    // 2. weight ring prologue, in slot order
-    const uint4 *pc = pcodes + lane;
-    const uint2 *ps = pscales + r;
+    // 2. weight ring prologue, in slot order.  The ring's loads are buffer
+    //    loads: one past the wave's last unit gets a descriptor of size 0,
+    //    which returns zeros without a memory access, so the loads stay
+    //    unconditional and no wave waits at the finish for data it never
+    //    uses.
+    const uint32_t cbytes = (uint32_t)((int64_t)a.NT * KTG * 1024);
+    const uint32_t sbytes = (uint32_t)((int64_t)a.NT * KTG * 128);
     uint4 cw[PF];
     uint2 sw[PF];
+    int ld_q = 0;                              // loads issued by this wave
     // next unit to load; loads past the wave's last unit re-read it, so the
     // ring stays unconditional.  With K ranges (KR) a unit's packed index is
     // t*KTG + c0 + c for (row tile t, range-local k-tile c), walked
     // incrementally; with one range it is the unit itself.
     int ld_u = u0, ld_t = KR && n > 0 ? u0 / KT : 0, ld_c = KR && n > 0 ? u0 - ld_t * KT : 0;
     auto load = [&](int s) {
-        const int64_t j = KR ? (int64_t)ld_t * KTG + c0 + ld_c : (int64_t)ld_u;
-        cw[s] = load_stream16(pc + j * 64);
-        sw[s] = ps[j * 16];
+        const uint32_t j = KR ? (uint32_t)(ld_t * KTG + c0 + ld_c) : (uint32_t)ld_u;
+        const bool live = ld_q < n;
+        ++ld_q;
+        const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint4 *>(pcodes), 0, (int)(live ? cbytes : 0u), 0x00020000),
+            lane * 16, j * 1024u, 2 /* non-temporal */);
+        cw[s] = make_uint4(c.x, c.y, c.z, c.w);
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(
+            __builtin_amdgcn_make_buffer_rsrc(const_cast<uint2 *>(pscales), 0, (int)(live ? sbytes : 0u), 0x00020000),
+            r * 8, j * 128u, 0);
+        sw[s] = make_uint2(v.x, v.y);
         if (KR) {
             if (ld_u < ulast) {
                 ++ld_u;
@@ -1025,12 +1038,13 @@ int64_t sk_ranges(int64_t M, int64_t K)
 }
 
 // The stream-K kernel serves a shape when its ranges' activations fit in LDS,
-// every range gets at least one k-tile, and unit indices stay below 2^31.
+// every range gets at least one k-tile, and the packed codes stay below
+// 4 GiB (32-bit buffer offsets: fewer than 2^22 units of 1 KB).
 bool sk_usable(int64_t M, int64_t N, int64_t K)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N), KS = sk_ranges(M, K);
     const int64_t KTR = (KT + KS - 1) / KS;
-    return M * KTR * 256 <= kSkXMaxBytes && KT - (KS - 1) * KTR >= 1 && NT * KT < ((int64_t)1 << 31);
+    return M * KTR * 256 <= kSkXMaxBytes && KT - (KS - 1) * KTR >= 1 && NT * KT < ((int64_t)1 << 22);
 }
 
 struct SkPlan {
