@@ -501,10 +501,12 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int gq = lane >> 4;
     const int G = a.G, WPG = a.WPG, KTG = a.KT, M = a.M, K = a.K;
 
-    // workgroups are dealt round-robin to the 8 XCDs: give consecutive ranges
-    // to workgroups on the same XCD
-    const int b = blockIdx.x;
-    const int LG = (G % 8 == 0) ? (b % 8) * (G / 8) + b / 8 : b;
+    // workgroup b takes the b-th range.  (Giving consecutive ranges to the
+    // workgroups of one XCD, so that exchange partners share an L2, measured
+    // 1-2.5% slower: the exchange words are device-scope atomics either way,
+    // and spreading each XCD's stream over the whole matrix serves HBM
+    // better.)
+    const int LG = blockIdx.x;
     // K range of this workgroup: k-tiles c0 .. c0 + KT - 1, streamed by the
     // GR workgroups of that range; below, units, KT and L are range-local
     const int GR = G / a.KS;
