@@ -195,8 +195,12 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
             const bool code = 8 * q + wave < TT;
             const uint8_t *base = code ? pcodes : pscales;
             const uint32_t bytes = live ? (code ? cbytes : sbytes) : 0u;
-            load_lds16(make_rsrc(base, bytes), sw + wlds[q], woff[q],
-                       (code ? (uint32_t)kTileCodeBytes : (uint32_t)kTileScaleBytes) * (uint32_t)c);
+            // the k-tile advance is wave-uniform; pinning it to a scalar register
+            // keeps the compiler from computing it per lane and wrapping the load
+            // in a loop over distinct values
+            const uint32_t adv = (uint32_t)__builtin_amdgcn_readfirstlane(
+                (int)((code ? (uint32_t)kTileCodeBytes : (uint32_t)kTileScaleBytes) * (uint32_t)c));
+            load_lds16(make_rsrc(base, bytes), sw + wlds[q], woff[q], adv);
         }
     };
     auto issue_stage = [&](int c, bool live, uint8_t *sx, uint8_t *sw) __attribute__((always_inline)) {

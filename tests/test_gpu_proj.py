@@ -97,12 +97,14 @@ RAGGED = {
     # (7, 4352, 640) .. (12, 5000, 3088) have more row tiles than a 256-CU
     # device has CUs and per-CU ranges that end inside row tiles: their split
     # row tiles are finished across workgroups, for every output row M can
-    # hold.  The last four cut K into 2, 4, 2 (ragged) and 8 ranges whose
-    # results are joined per output.
+    # hold.  (7, 200, 17408) .. (16, 1000, 32768) cut K into 2, 4, 2 (ragged)
+    # and 8 ranges whose results are joined per output.  The last three need
+    # more than 8 ranges and run on the split kernel (activation pieces in
+    # the register ring): M > 8, M = 1 and M = 3.
     "gemv": [(5, 1000, 1040), (16, 272, 2000), (1, 3, 4112), (7, 33, 144), (3, 4097, 128),
              (12, 130, 9216), (7, 4352, 640), (2, 6000, 272), (16, 4368, 912),
              (12, 5000, 3088), (7, 200, 17408), (16, 272, 16384), (9, 4352, 8320),
-             (16, 1000, 32768)],
+             (16, 1000, 32768), (16, 300, 33024), (1, 100, 1048576), (3, 40, 200000)],
     "gemm": [(129, 300, 1040), (513, 100, 272), (1, 17, 5136), (200, 4112, 128),
              (64, 2049, 400), (300, 48, 2000)],
 }
