@@ -361,7 +361,8 @@ gemv_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
 }
 
 // ---------------------------------------------------------------------------
-// Stream-K variant, used whenever the activations fit in LDS.
+// Stream-K variant, used whenever the activations of at most 8 K ranges fit
+// in LDS and the packed codes stay below 4 GiB (32-bit buffer offsets).
 //
 // The k-tiles of all row tiles, in packed-memory order (row tile t, k-tile c
 // at unit t*KT + c), are dealt out in equal contiguous ranges: G workgroups,
