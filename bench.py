@@ -33,7 +33,9 @@ Also measured and reported in the same JSON line:
                 34816 x 5120 and lm-head 248320 x 5120): algorithmic bytes
                 (bf16 in, codes + scales out) / s; two launches, the first
                 reads w for its max, the second reads it again to quantize.
-  cpu_baseline  the CPU oracle on the decode step, on the host cores.
+  cpu_baseline  the CPU oracle on the decode step, on the host cores, and on
+                one thread for the tiny case, the decode step and the 4B pair.
+  device_state_before_timing  rocm-smi's clocks and GPU processes (idle check).
 """
 from __future__ import annotations
 
@@ -108,6 +110,46 @@ def timed_region(torch, launches, steps):
     return t0.elapsed_time(t1) / steps, host_s
 
 
+def single_thread_oracle(oracle, synth, dec):
+    """The oracle on one host thread: the 512 x 256 tiny case (median of 3
+    runs), one decode step (gate/up + down, one run) and the 4B-style
+    up/down pair (one run each); seconds and algorithmic GB/s."""
+    res = {}
+
+    def run(cases, reps):
+        times = []
+        for _ in range(reps):
+            t = time.perf_counter()
+            for c in cases:
+                oracle.proj(c.matrix.codes, c.matrix.scales, c.matrix.g, c.x, nthreads=1)
+            times.append(time.perf_counter() - t)
+        el = sorted(times)[len(times) // 2]
+        b = sum(algo_bytes(c.M, c.N, c.K) for c in cases)
+        return {"s": round(el, 4), "gbs": round(b / el / 1e9, 4)}
+
+    res["tiny_512x256_M1"] = run(synth.workload_cases("tiny"), 3)
+    res["decode_step_M1"] = run(dec, 1)
+    for c in synth.workload_cases("lmh", only=["up_4b", "down_4b"]):
+        res[f"{c.name}_{c.N}x{c.K}_M1"] = run([c], 1)
+    return res
+
+
+def device_state():
+    """Clocks and GPU processes as rocm-smi reports them just before timing
+    (an idle check: no other process should hold the GPU); None fields when
+    rocm-smi is unavailable."""
+    import subprocess
+    state = {}
+    for key, flag in (("clocks", "--showclocks"), ("pids", "--showpids")):
+        try:
+            r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True,
+                               timeout=30)
+            state[key] = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip() else None
+        except (OSError, subprocess.SubprocessError, ValueError):
+            state[key] = None
+    return state
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -127,6 +169,8 @@ def main():
               "(the projection shards by output columns or by k; see DESIGN.md).",
               file=sys.stderr)
         sys.exit(2)
+
+    smi = device_state()
 
     import numpy as np
     import torch
@@ -158,7 +202,7 @@ def main():
         pc, ps = u["w"][i % len(u["w"])]
         return lambda: fn(pc, ps, u["g"], u["x"], u["y"], c.M, c.N, c.K)
 
-    out = {"metric": METRIC}
+    out = {"metric": METRIC, "device_state_before_timing": smi}
 
     # ---- decode step: gate/up + down GEMV at M = 1 -------------------------
     dec = synth.workload_cases("dec")
@@ -435,7 +479,8 @@ def main():
                                "cores": nthreads, "kind": "oracle",
                                "sample": f"{reps} full decode steps (gate/up + down, M=1, "
                                          f"all rows) in {el:.2f} s, fp64",
-                               "tokens_per_s": round(reps / el, 2)}
+                               "tokens_per_s": round(reps / el, 2),
+                               "single_thread": single_thread_oracle(oracle, synth, dec)}
 
     print(json.dumps(out), flush=True)
 
