@@ -139,14 +139,22 @@ def device_state():
     (an idle check: no other process should hold the GPU); None fields when
     rocm-smi is unavailable."""
     import subprocess
-    state = {}
-    for key, flag in (("clocks", "--showclocks"), ("pids", "--showpids")):
-        try:
-            r = subprocess.run(["rocm-smi", flag, "--json"], capture_output=True, text=True,
-                               timeout=30)
-            state[key] = json.loads(r.stdout) if r.returncode == 0 and r.stdout.strip() else None
-        except (OSError, subprocess.SubprocessError, ValueError):
-            state[key] = None
+    state = {"clocks": None, "pids": None}
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
+                           text=True, timeout=30)
+        if r.returncode == 0 and r.stdout.strip():
+            state["clocks"] = json.loads(r.stdout)
+        # the process list as printed (its JSON form is empty when no process
+        # holds the GPU)
+        r = subprocess.run(["rocm-smi", "--showpids"], capture_output=True, text=True,
+                           timeout=30)
+        if r.returncode == 0:
+            state["pids"] = [ln.strip() for ln in r.stdout.splitlines()
+                             if ln.strip() and not set(ln.strip()) <= set("=-")
+                             and "ROCm System Management" not in ln]
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
     return state
 
 
