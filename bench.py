@@ -35,7 +35,8 @@ Also measured and reported in the same JSON line:
                 reads w for its max, the second reads it again to quantize.
   cpu_baseline  the CPU oracle on the decode step, on the host cores, and on
                 one thread for the tiny case, the decode step and the 4B pair.
-  device_state_before_timing  rocm-smi's clocks and GPU processes (idle check).
+  device_state_before_timing  clock levels and the processes holding a GPU
+                (idle check), from sysfs.
 """
 from __future__ import annotations
 
@@ -135,25 +136,30 @@ def single_thread_oracle(oracle, synth, dec):
 
 
 def device_state():
-    """Clocks and GPU processes as rocm-smi reports them just before timing
-    (an idle check: no other process should hold the GPU); None fields when
-    rocm-smi is unavailable."""
-    import subprocess
-    state = {"clocks": None, "pids": None}
+    """Shader and memory clock levels and the processes holding a GPU, read
+    from sysfs just before timing (an idle check: no other process should
+    hold the GPU).  No child process is started: under a profiler every
+    process inherits its preloaded library, which initialises the GPU."""
+    import glob
+    state = {"clocks": {}, "gpu_pids": None}
+    for card in sorted(glob.glob("/sys/class/drm/card[0-9]*/device")):
+        try:
+            if open(os.path.join(card, "vendor")).read().strip() != "0x1002":
+                continue
+            levels = {}
+            for clk in ("sclk", "mclk"):
+                lines = open(os.path.join(card, f"pp_dpm_{clk}")).read().split("\n")
+                cur = [ln for ln in lines if ln.strip().endswith("*")]
+                levels[clk] = {"current": cur[0].split(":", 1)[1].strip(" *") if cur else None,
+                               "levels": [ln.split(":", 1)[1].strip(" *") for ln in lines
+                                          if ":" in ln]}
+            state["clocks"][os.path.basename(os.path.dirname(card))] = levels
+        except (OSError, IndexError):
+            continue
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True,
-                           text=True, timeout=30)
-        if r.returncode == 0 and r.stdout.strip():
-            state["clocks"] = json.loads(r.stdout)
-        # the process list as printed (its JSON form is empty when no process
-        # holds the GPU)
-        r = subprocess.run(["rocm-smi", "--showpids"], capture_output=True, text=True,
-                           timeout=30)
-        if r.returncode == 0:
-            state["pids"] = [ln.strip() for ln in r.stdout.splitlines()
-                             if ln.strip() and not set(ln.strip()) <= set("=-")
-                             and "ROCm System Management" not in ln]
-    except (OSError, subprocess.SubprocessError, ValueError):
+        state["gpu_pids"] = sorted(int(p) for p in os.listdir("/sys/class/kfd/kfd/proc")
+                                   if p.isdigit() and int(p) != os.getpid())
+    except OSError:
         pass
     return state
 
