@@ -33,6 +33,8 @@ Also measured and reported in the same JSON line:
                 34816 x 5120 and lm-head 248320 x 5120): algorithmic bytes
                 (bf16 in, codes + scales out) / s; two launches, the first
                 reads w for its max, the second reads it again to quantize.
+  graph_replay  the decode step captured as a HIP graph and replayed (the
+                launch path a serving loop would use).
   cpu_baseline  the CPU oracle on the decode step, on the host cores, and on
                 one thread for the tiny case, the decode step and the 4B pair.
   device_state_before_timing  clock levels and the processes holding a GPU
@@ -164,6 +166,31 @@ def device_state():
     return state
 
 
+def graph_replay(torch, launches, steps_per_pass, passes):
+    """`launches` (steps_per_pass steps) captured once as a HIP graph and
+    replayed `passes` times back to back behind a head start.  Returns (ms
+    per step, host microseconds per replay call)."""
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for fn in launches:
+            fn()
+    torch.cuda.synchronize()
+    graph.replay()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    head_start(torch, 0.05 * len(launches) * passes + 5)
+    h0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(passes):
+        graph.replay()
+    t1.record(stream)
+    host_us = (time.perf_counter() - h0) / passes * 1e6
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / (passes * steps_per_pass), host_us
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,6 +295,18 @@ def main():
             "wall_s_timed": round(wall, 4),
             "host_enqueue_us_per_launch": round(host_s / (args.steps * len(dec_u)) * 1e6, 2),
         })
+        # the same step as a captured graph: one pass over every weight copy
+        # (ncopy steps) per graph, replayed back to back
+        passes = max(1, args.steps // ncopy)
+        g_ms, g_host = graph_replay(
+            torch, [launcher("gemv", u, i) for i in range(ncopy) for u in dec_u], ncopy, passes)
+        out["graph_replay"] = {
+            "ms_per_step": round(g_ms, 5), "steps": passes * ncopy,
+            "gbs": round(step_bytes / (g_ms * 1e-3) / 1e9, 1),
+            "launches_per_graph": ncopy * len(dec_u),
+            "host_us_per_replay": round(g_host, 2),
+            "note": "the decode step captured as a HIP graph (torch.cuda.CUDAGraph over the "
+                    "C-ABI calls, caller-owned buffers, no allocation per call)"}
 
     # ---- prefill chunk: M = 512 GEMM --------------------------------------
     if args.only in ("pre", "all"):
