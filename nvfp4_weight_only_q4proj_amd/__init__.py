@@ -16,7 +16,9 @@ fp32 y and fp32 global scale g.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
+import functools
 import os
 
 import torch
@@ -97,35 +99,62 @@ def library():
     return _lib
 
 
+@functools.lru_cache(maxsize=4096)
 def q4proj_packed_codes_bytes(N: int, K: int) -> int:
     return int(_lib.q4proj_packed_codes_bytes(N, K))
 
 
+@functools.lru_cache(maxsize=4096)
 def q4proj_packed_scales_bytes(N: int, K: int) -> int:
     return int(_lib.q4proj_packed_scales_bytes(N, K))
 
 
+@functools.lru_cache(maxsize=4096)
 def q4proj_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(_lib.q4proj_workspace_bytes(M, N, K))
 
 
+@functools.lru_cache(maxsize=4096)
 def q4proj_silu_mul_workspace_bytes(M: int, F: int, K: int) -> int:
     return int(_lib.q4proj_silu_mul_workspace_bytes(M, F, K))
 
 
-def _stream(t: torch.Tensor, stream):
+# The checks below sit on the decode path (one call per projection, ~12 us of
+# GPU time each), so they use the cheap tensor queries: device indices rather
+# than torch.device objects, the raw current-stream handle, and no device
+# switch when the tensors are on the current device.
+_SAME_DEVICE = contextlib.nullcontext()
+
+
+def _dev(t, name: str) -> int:
+    """Index of the HIP device holding tensor t."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    d = t.get_device()
+    if d < 0:
+        raise ValueError(f"{name} must be on a HIP device, got {t.device}")
+    return d
+
+
+def _guard(dev: int):
+    """Make device dev current for the call (a no-op when it already is)."""
+    return _SAME_DEVICE if torch._C._cuda_getDevice() == dev else torch.cuda.device(dev)
+
+
+def _stream(dev: int, stream):
+    """hipStream_t of `stream`, or of device dev's current stream."""
     if stream is None:
-        stream = torch.cuda.current_stream(t.device)
-    return ctypes.c_void_p(stream.cuda_stream)
+        return torch._C._cuda_getCurrentRawStream(dev)
+    return stream.cuda_stream
 
 
-def _need(t: torch.Tensor, name: str, dtype, numel: int, device):
+def _need(t: torch.Tensor, name: str, dtype, numel: int, dev: int):
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch.Tensor")
     if t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if t.device.type != "cuda" or (device is not None and t.device != device):
-        raise ValueError(f"{name} must be on {device or 'a HIP device'}, got {t.device}")
+    if t.get_device() != dev:
+        raise ValueError(f"{name} must be on cuda:{dev}, got {t.device}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if t.numel() != numel:
@@ -136,26 +165,26 @@ def q4proj_pack(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int,
                 packed_codes: torch.Tensor, packed_scales: torch.Tensor, stream=None) -> None:
     """codes u8 [N][K/2], scales u8 [N][K/16] -> packed buffers (u8, sizes from
     q4proj_packed_*_bytes)."""
-    dev = codes.device
+    dev = _dev(codes, "codes")
     _need(codes, "codes", torch.uint8, N * (K // 2), dev)
     _need(scales, "scales", torch.uint8, N * (K // 16), dev)
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
-    with torch.cuda.device(dev):
+    with _guard(dev):
         _check(_lib.q4proj_pack(codes.data_ptr(), scales.data_ptr(), N, K, packed_codes.data_ptr(),
-                                packed_scales.data_ptr(), _stream(codes, stream)), "q4proj_pack")
+                                packed_scales.data_ptr(), _stream(dev, stream)), "q4proj_pack")
 
 
 def q4proj_unpack(packed_codes: torch.Tensor, packed_scales: torch.Tensor, N: int, K: int,
                   codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
-    dev = packed_codes.device
+    dev = _dev(packed_codes, "packed_codes")
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
     _need(codes, "codes", torch.uint8, N * (K // 2), dev)
     _need(scales, "scales", torch.uint8, N * (K // 16), dev)
-    with torch.cuda.device(dev):
+    with _guard(dev):
         _check(_lib.q4proj_unpack(packed_codes.data_ptr(), packed_scales.data_ptr(), N, K,
-                                  codes.data_ptr(), scales.data_ptr(), _stream(codes, stream)),
+                                  codes.data_ptr(), scales.data_ptr(), _stream(dev, stream)),
                "q4proj_unpack")
 
 
@@ -168,8 +197,9 @@ def default_workspace(device, nbytes: int):
     that may run concurrently on one device need workspaces of their own."""
     if nbytes <= 0:
         return None
-    key = torch.device(device).index if torch.device(device).index is not None else \
-        torch.cuda.current_device()
+    key = device if isinstance(device, int) else (
+        torch.device(device).index if torch.device(device).index is not None
+        else torch.cuda.current_device())
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
         ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", key))
@@ -187,7 +217,7 @@ def _bf16_bits(t, name):
 
 
 def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, workspace, stream):
-    dev = x.device
+    dev = _dev(x, "x")
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
     x = _bf16_bits(x, "x")
@@ -199,9 +229,9 @@ def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, w
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    with torch.cuda.device(dev):
+    with _guard(dev):
         _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
-                  x.data_ptr(), y.data_ptr(), M, N, K, ws_ptr, ws_bytes, _stream(x, stream)),
+                  x.data_ptr(), y.data_ptr(), M, N, K, ws_ptr, ws_bytes, _stream(dev, stream)),
                where)
 
 
@@ -236,7 +266,7 @@ def q4proj_gemm_silu_mul(packed_codes, packed_scales, global_scale: float, x, h,
 
 def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, K, workspace,
               stream):
-    dev = x.device
+    dev = _dev(x, "x")
     N = 2 * F
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
@@ -250,12 +280,13 @@ def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, 
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    with torch.cuda.device(dev):
+    with _guard(dev):
         _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
-                  x.data_ptr(), h.data_ptr(), M, F, K, ws_ptr, ws_bytes, _stream(x, stream)),
+                  x.data_ptr(), h.data_ptr(), M, F, K, ws_ptr, ws_bytes, _stream(dev, stream)),
                where)
 
 
+@functools.lru_cache(maxsize=4096)
 def q4proj_argmax_workspace_bytes(M: int, N: int, K: int) -> int:
     return int(_lib.q4proj_argmax_workspace_bytes(M, N, K))
 
@@ -264,7 +295,7 @@ def q4proj_gemv_argmax(packed_codes, packed_scales, global_scale: float, x, y, m
                        M: int, N: int, K: int, workspace=None, stream=None) -> None:
     """Greedy argmax of each row of the logits x . dequant(W)^T (1 <= M <= 16):
     max_val float32 [M], max_idx int64 [M]; y (fp32 [M][N]) may be None."""
-    dev = x.device
+    dev = _dev(x, "x")
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
     x = _bf16_bits(x, "x")
@@ -279,12 +310,12 @@ def q4proj_gemv_argmax(packed_codes, packed_scales, global_scale: float, x, y, m
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    with torch.cuda.device(dev):
+    with _guard(dev):
         _check(_lib.q4proj_gemv_argmax(packed_codes.data_ptr(), packed_scales.data_ptr(),
                                        float(global_scale), x.data_ptr(),
                                        None if y is None else y.data_ptr(), max_val.data_ptr(),
                                        max_idx.data_ptr(), M, N, K, ws_ptr, ws_bytes,
-                                       _stream(x, stream)), "q4proj_gemv_argmax")
+                                       _stream(dev, stream)), "q4proj_gemv_argmax")
 
 
 def q4proj_quantize_workspace_bytes(N: int, K: int) -> int:
@@ -296,7 +327,7 @@ def q4proj_quantize(w, N: int, K: int, codes: torch.Tensor, scales: torch.Tensor
     """bf16 w [N][K] -> codes u8 [N][K/2], scales u8 [N][K/16], global_scale
     (a one-element float32 device tensor)."""
     w = _bf16_bits(w, "w")
-    dev = w.device
+    dev = _dev(w, "w")
     _need(w, "w", w.dtype, N * K, dev)
     _need(codes, "codes", torch.uint8, N * (K // 2), dev)
     _need(scales, "scales", torch.uint8, N * (K // 16), dev)
@@ -305,10 +336,10 @@ def q4proj_quantize(w, N: int, K: int, codes: torch.Tensor, scales: torch.Tensor
         workspace = torch.empty(q4proj_quantize_workspace_bytes(N, K), dtype=torch.uint8,
                                 device=dev)
     _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
-    with torch.cuda.device(dev):
+    with _guard(dev):
         _check(_lib.q4proj_quantize(w.data_ptr(), N, K, codes.data_ptr(), scales.data_ptr(),
                                     global_scale.data_ptr(), workspace.data_ptr(),
-                                    workspace.numel(), _stream(w, stream)), "q4proj_quantize")
+                                    workspace.numel(), _stream(dev, stream)), "q4proj_quantize")
 
 
 def quantize_weight(w, N: int, K: int, stream=None):
