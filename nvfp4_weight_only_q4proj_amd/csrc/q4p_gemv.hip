@@ -2,7 +2,16 @@
 //
 // At M = 1..16 every weight byte feeds at most 16 multiply-adds, so the
 // kernel is bound by streaming the packed weight from HBM once (0.5625 bytes
-// per weight).  Design:
+// per weight).  Two kernels share the per-block arithmetic (gemv_half):
+//
+//  * gemv_sk_kernel, the stream-K kernel further down: every CU streams an
+//    equal contiguous range of the k-tiles of all row tiles.  It serves every
+//    shape whose activations of at most 8 K ranges fit in LDS and whose
+//    packed codes stay below 4 GiB: all the decode, verify and lm-head shapes.
+//  * gemv_kernel, the split kernel described next, for the remaining shapes
+//    (M*K beyond the LDS budget, or codes of 4 GiB and more).
+//
+// Split kernel:
 //
 //  * A workgroup owns TB 16-row tiles of W; S waves per tile split its
 //    k-tiles into contiguous ranges (split-K inside the workgroup), and the
