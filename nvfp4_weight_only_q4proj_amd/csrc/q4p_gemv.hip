@@ -509,6 +509,12 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int lane = threadIdx.x & 63;
     const int r = lane & 15;
     const int gq = lane >> 4;
+    // Output rows of a lane: the MFMA gives lane (r, gq) the rows 4gq..4gq+3
+    // of A.  With ROWS <= 2 (M <= 8) activation row m is placed at A row
+    // 4*(m/2) + m%2, so the live rows are 2gq and 2gq+1 and the per-block scale
+    // costs two fmas per lane instead of four; with ROWS = 4 A row i is row i.
+    constexpr bool COMPACT = ROWS <= 2;
+    auto out_row = [](int q, int j) { return COMPACT ? 2 * q + j : 4 * q + j; };
     const int G = a.G, WPG = a.WPG, KTG = a.KT, M = a.M, K = a.K;
 
     // workgroup b takes the b-th range.  (Giving consecutive ranges to the
@@ -654,8 +660,10 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     __syncthreads();
 
     // 4. stream this wave's units
-    const uint8_t *xls = (r < M) ? xl + (r * KT * 4 + gq) * 64 : zstrip;
-    const int xstep = (r < M) ? 256 : 0;
+    const int xr = COMPACT ? 2 * (r >> 2) + (r & 1) : r;      // activation row of A row r
+    const bool xlive = (!COMPACT || (r & 2) == 0) && xr < M;
+    const uint8_t *xls = xlive ? xl + (xr * KT * 4 + gq) * 64 : zstrip;
+    const int xstep = xlive ? 256 : 0;
     const float g = a.g;
     const int N = a.N;
     const int tfirst = n > 0 ? u0 / KT : 0;
@@ -716,7 +724,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             const int f = 8 * tt + r;
 #pragma unroll
             for (int j = 0; j < ROWS; ++j) {
-                const int m = 4 * gq + j;
+                const int m = out_row(gq, j);
                 // copy the element out first: clang mis-lowers a bit_cast whose
                 // operand is a vector element (it reads element 0)
                 const float vg = v[j];
@@ -730,7 +738,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
         if (col < N) {
 #pragma unroll
             for (int j = 0; j < ROWS; ++j) {
-                const int m = 4 * gq + j;
+                const int m = out_row(gq, j);
                 const float vj = v[j];
                 if (m < M)
                     join(m, col, vj, j);
@@ -816,7 +824,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
         if (SILU) {
 #pragma unroll
             for (int j = 0; j < ROWS; ++j) {
-                const int m = 4 * gq + j;
+                const int m = out_row(gq, j);
                 const float sg = sum[j];
                 const float su = swap8(sg);
                 if (r < 8 && m < M) {
@@ -834,7 +842,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
         const int col = 16 * tau + r;
 #pragma unroll
         for (int j = 0; j < ROWS; ++j) {
-            const int m = 4 * gq + j;
+            const int m = out_row(gq, j);
             if (m < M) {
                 // copy the element out first: clang mis-lowers a bit_cast whose
                 // operand is a vector element (it reads element 0)
@@ -868,7 +876,7 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
                 k = o > k ? o : k;
             }
             if (r == 0)
-                red[wave * 16 + 4 * gq + j] = k;
+                red[wave * 16 + out_row(gq, j)] = k;
         }
         __syncthreads();
         if ((int)threadIdx.x < M) {
@@ -1015,12 +1023,10 @@ typedef void (*gemv_sk_fn)(const uint4 *, const uint2 *, const uint16_t *, void 
 template <bool KR, int EPI>
 gemv_sk_fn pick_sk_kernel_k(int64_t M)
 {
-    switch (M) {
-    case 1: return gemv_sk_kernel<1, kSkPrefetch, KR, EPI>;
-    case 2: return gemv_sk_kernel<2, kSkPrefetch, KR, EPI>;
-    case 3: return gemv_sk_kernel<3, kSkPrefetch, KR, EPI>;
-    default: return gemv_sk_kernel<4, kSkPrefetch, KR, EPI>;
-    }
+    // two live rows per lane up to M = 8 (rows placed two per group of four)
+    return M == 1 ? gemv_sk_kernel<1, kSkPrefetch, KR, EPI>
+         : M <= 8 ? gemv_sk_kernel<2, kSkPrefetch, KR, EPI>
+                  : gemv_sk_kernel<4, kSkPrefetch, KR, EPI>;
 }
 
 template <int EPI>

@@ -67,6 +67,16 @@ def test_small_shapes(M, N, K):
     check(mat, x)
 
 
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_every_m(M):
+    """Every M from 1 to 16 over 4352 x 640 (row tiles split between waves and
+    workgroups) and 300 x K with two K ranges."""
+    for j, (N, K) in enumerate([(4352, 640), (300, 128 * (512 // M + 4))]):
+        mat = synth.nvfp4_normal_matrix(130 + M, 1 + j, N, K)
+        x = synth.x_bf16(130 + j, M, M, K)
+        check(mat, x)
+
+
 def test_logits_equal_plain_gemv():
     mat = synth.nvfp4_normal_matrix(120, 1, 20000, 3072)
     x = synth.x_bf16(120, 1, 5, 3072)

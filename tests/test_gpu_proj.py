@@ -119,6 +119,20 @@ def test_ragged_shapes(kind):
         assert_parity(m.codes, m.scales, m.g, x, y)
 
 
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_gemv_every_m(M):
+    """Every M of the decode/verify range on two shapes: 4352 x 640 (272 row
+    tiles over one workgroup per CU, so row tiles are split between waves and
+    between workgroups) and 300 x K with two K ranges (the activations of all
+    of K exceed one range's LDS).  Each M places its rows differently in the
+    lanes' output slots (two per lane up to M = 8, four above)."""
+    for j, (N, K) in enumerate([(4352, 640), (300, 128 * (512 // M + 4))]):
+        m = synth.nvfp4_normal_matrix(60 + M, 3 + j, N, K)
+        x = synth.x_bf16(60 + M, 4 + j, M, K)
+        y = run("gemv", m.codes, m.scales, m.g, x)
+        assert_parity(m.codes, m.scales, m.g, x, y)
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_nan_and_zero_scales(kind):
     codes, scales, x = pins.tiny_inputs(7, 40, 96, 77)

@@ -56,6 +56,18 @@ def test_small_shapes(M, F, K):
     assert_silu_parity(mat, x, F, h)
 
 
+@pytest.mark.parametrize("M", list(range(1, 17)))
+def test_every_m(M):
+    """Every M from 1 to 16: F = 2176 (272 row tiles, split between waves and
+    workgroups) at K = 640, and F = 152 with two K ranges."""
+    for j, (F, K) in enumerate([(2176, 640), (152, 128 * (512 // M + 4))]):
+        mat = fused_matrix(70 + M + 20 * j, F, K)
+        x = synth.x_bf16(70 + j, M, M, K)
+        note(f"gemv_silu_mul M={M} F={F} K={K}")
+        h = run_fused(pack(mat.codes, mat.scales, 2 * F, K), mat.g, x, F, K)
+        assert_silu_parity(mat, x, F, h)
+
+
 # Many row tiles per wave at short K (tiles complete inside one wave), and one
 # shape with two K ranges.
 WHOLE = [(1, 32768, 128), (3, 49152, 128), (4, 16384, 256), (16, 8192, 384), (2, 24592, 256),
