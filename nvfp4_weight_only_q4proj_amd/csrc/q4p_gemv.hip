@@ -510,11 +510,11 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int r = lane & 15;
     const int gq = lane >> 4;
     // Output rows of a lane: the MFMA gives lane (r, gq) the rows 4gq..4gq+3
-    // of A.  With ROWS <= 2 (M <= 8) activation row m is placed at A row
-    // 4*(m/2) + m%2, so the live rows are 2gq and 2gq+1 and the per-block scale
-    // costs two fmas per lane instead of four; with ROWS = 4 A row i is row i.
-    constexpr bool COMPACT = ROWS <= 2;
-    auto out_row = [](int q, int j) { return COMPACT ? 2 * q + j : 4 * q + j; };
+    // of A.  With ROWS = ceil(M/4) activation row m is placed at A row
+    // 4*(m/ROWS) + m%ROWS, so a lane's live rows are its first ROWS slots,
+    // ROWS*gq + j, and the per-block scale costs ROWS fmas per lane instead
+    // of four (ROWS = 4, M > 12: A row i is row i).
+    auto out_row = [](int q, int j) { return ROWS * q + j; };
     const int G = a.G, WPG = a.WPG, KTG = a.KT, M = a.M, K = a.K;
 
     // workgroup b takes the b-th range.  (Giving consecutive ranges to the
@@ -660,8 +660,8 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     __syncthreads();
 
     // 4. stream this wave's units
-    const int xr = COMPACT ? 2 * (r >> 2) + (r & 1) : r;      // activation row of A row r
-    const bool xlive = (!COMPACT || (r & 2) == 0) && xr < M;
+    const int xr = ROWS * (r >> 2) + (r & 3);                  // activation row of A row r
+    const bool xlive = (r & 3) < ROWS && xr < M;
     const uint8_t *xls = xlive ? xl + (xr * KT * 4 + gq) * 64 : zstrip;
     const int xstep = xlive ? 256 : 0;
     const float g = a.g;
@@ -1023,10 +1023,11 @@ typedef void (*gemv_sk_fn)(const uint4 *, const uint2 *, const uint16_t *, void 
 template <bool KR, int EPI>
 gemv_sk_fn pick_sk_kernel_k(int64_t M)
 {
-    // two live rows per lane up to M = 8 (rows placed two per group of four)
-    return M == 1 ? gemv_sk_kernel<1, kSkPrefetch, KR, EPI>
+    // ceil(M/4) live rows per lane (rows placed that many per group of four)
+    return M <= 4 ? gemv_sk_kernel<1, kSkPrefetch, KR, EPI>
          : M <= 8 ? gemv_sk_kernel<2, kSkPrefetch, KR, EPI>
-                  : gemv_sk_kernel<4, kSkPrefetch, KR, EPI>;
+         : M <= 12 ? gemv_sk_kernel<3, kSkPrefetch, KR, EPI>
+                   : gemv_sk_kernel<4, kSkPrefetch, KR, EPI>;
 }
 
 template <int EPI>
