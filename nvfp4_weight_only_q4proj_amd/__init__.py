@@ -124,6 +124,9 @@ def q4proj_silu_mul_workspace_bytes(M: int, F: int, K: int) -> int:
 # than torch.device objects, the raw current-stream handle, and no device
 # switch when the tensors are on the current device.
 _SAME_DEVICE = contextlib.nullcontext()
+# torch's own fast accessors (private; the public calls are the fallback)
+_raw_stream = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+_cur_device = getattr(torch._C, "_cuda_getDevice", None) or torch.cuda.current_device
 
 
 def _dev(t, name: str) -> int:
@@ -138,13 +141,15 @@ def _dev(t, name: str) -> int:
 
 def _guard(dev: int):
     """Make device dev current for the call (a no-op when it already is)."""
-    return _SAME_DEVICE if torch._C._cuda_getDevice() == dev else torch.cuda.device(dev)
+    return _SAME_DEVICE if _cur_device() == dev else torch.cuda.device(dev)
 
 
 def _stream(dev: int, stream):
     """hipStream_t of `stream`, or of device dev's current stream."""
     if stream is None:
-        return torch._C._cuda_getCurrentRawStream(dev)
+        if _raw_stream is not None:
+            return _raw_stream(dev)
+        stream = torch.cuda.current_stream(dev)
     return stream.cuda_stream
 
 
