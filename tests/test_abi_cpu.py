@@ -248,3 +248,17 @@ def test_no_device_no_fallback(q4):
     assert lib.q4proj_gemv_argmax(A, B, ctypes.c_float(1.0), X, None, W + (1 << 20),
                                   W + (1 << 20) + 4096, 1, 64, 256, W, 512 * 1024 + 16,
                                   None) == q4.EDEVICE
+
+
+def test_plain_c_consumer_builds(tmp_path):
+    """The plain C consumer of the ABI (run on the GPU by test_gpu_c_abi.py)
+    compiles against include/q4proj.h and links the library."""
+    import importlib.util
+    import os
+    here = os.path.dirname(os.path.abspath(__file__))
+    spec = importlib.util.spec_from_file_location("c_abi_build", os.path.join(here, "c_abi", "build.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    out = mod.build(out=str(tmp_path / "libabi_consumer.so"))
+    # not loaded here: its run paths are relative to tests/c_abi/
+    assert b"abi_consumer_run" in open(out, "rb").read()
