@@ -110,7 +110,7 @@ template <int Q, int RT, bool SILU>
 __global__ void __launch_bounds__(512)
 gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ pscales, float g,
             const uint16_t *__restrict__ x, void *__restrict__ out, int M, int N, int64_t ldy,
-            int K, int KT, int NT)
+            int K, int KT, int NT, int buf_out)
 {
     constexpr int TT = 4 * Q + RT;                         // tiles per workgroup (== T)
     constexpr int RB = RT == 2 ? 1 : RT;                   // remaining-tile operands per wave
@@ -393,42 +393,129 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
 
     // ---- epilogue: lane (r, gq) holds rows 4*gq + i of each 16-row block ----
     if (SILU) {
-        uint16_t *h = static_cast<uint16_t *>(out);
-        const bool hi = r >= 8;
-        // tile t, rows mrow + 0..3 (mrow = m0 + 16*block + 4*gq): outputs
-        // f = 8t + r%8; called with the wave's lanes all active
-        auto put = [&](int t, int mrow, const floatx4_t &v) __attribute__((always_inline)) {
-            const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-            const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
-            const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
-            const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
-            const int m = mrow + (hi ? 2 : 0);
-            const int64_t f = 8 * (int64_t)t + (r & 7);
-            if (m < M)
-                h[(int64_t)m * ldy + f] = silu_mul_bf16(g * ga, g * ua);
-            if (m + 1 < M)
-                h[(int64_t)(m + 1) * ldy + f] = silu_mul_bf16(g * gb, g * ub);
+        if (buf_out) {
+            // bf16 h through buffer stores as y below (2 bytes per output, rows
+            // past M dropped at the buffer's end)
+            const uint32_t hstride = (uint32_t)ldy * 2u;        // bytes per row of h
+            const __amdgpu_buffer_rsrc_t hrs = make_rsrc(out, (uint32_t)M * hstride);
+            const bool hi = r >= 8;
+            // lanes r < 8 write rows 4gq, 4gq+1 of a block, lanes r >= 8 rows
+            // 4gq+2, 4gq+3; output f = 8t + r%8
+            const uint32_t lane_row = (uint32_t)(4 * gq + (hi ? 2 : 0)) * hstride;
+            // tile t, block rows starting at the wave-uniform mrow; called with
+            // the wave's lanes all active
+            auto put = [&](int t, int mrow, const floatx4_t &v) __attribute__((always_inline)) {
+                const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+                const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
+                const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
+                const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
+                const uint32_t f = 8u * (uint32_t)t + (uint32_t)(r & 7);
+                const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)mrow * hstride));
+                const uint32_t off = lane_row + f * 2u + row;
+                __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * ga, g * ua), hrs, (int)off, 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * gb, g * ub), hrs,
+                                                      (int)(off + hstride), 0, 0);
+            };
+#pragma unroll
+            for (int j = 0; j < Q; ++j) {
+                const int t = tile0 + w * Q + j;
+                if (t < NT) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        put(t, m0 + 16 * (i ^ rb), accF[j][i]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
+                if (t < NT) {
+#pragma unroll
+                    for (int i = 0; i < RR; ++i)
+                        put(t, m0 + 16 * (rb + i), accR[j][i]);
+                }
+            }
+        } else {
+            // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
+            uint16_t *h = static_cast<uint16_t *>(out);
+            const bool hi = r >= 8;
+            // tile t, rows mrow + 0..3 (mrow = m0 + 16*block + 4*gq): outputs
+            // f = 8t + r%8; called with the wave's lanes all active
+            auto put = [&](int t, int mrow, const floatx4_t &v) __attribute__((always_inline)) {
+                const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+                const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
+                const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
+                const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
+                const int m = mrow + (hi ? 2 : 0);
+                const int64_t f = 8 * (int64_t)t + (r & 7);
+                if (m < M)
+                    h[(int64_t)m * ldy + f] = silu_mul_bf16(g * ga, g * ua);
+                if (m + 1 < M)
+                    h[(int64_t)(m + 1) * ldy + f] = silu_mul_bf16(g * gb, g * ub);
+            };
+#pragma unroll
+            for (int j = 0; j < Q; ++j) {
+                const int t = tile0 + w * Q + j;
+                if (t < NT) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i)
+                        put(t, m0 + 16 * (i ^ rb) + 4 * gq, accF[j][i]);
+                }
+            }
+#pragma unroll
+            for (int j = 0; j < RB; ++j) {
+                const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
+                if (t < NT) {
+#pragma unroll
+                    for (int i = 0; i < RR; ++i)
+                        put(t, m0 + 16 * (rb + i) + 4 * gq, accR[j][i]);
+                }
+            }
+        }
+        return;
+    }
+    if (buf_out) {
+        // y through buffer stores: the row part of each offset is wave-uniform
+        // and the lane part fixed, so a store costs one add.  Rows past M lie
+        // past the end of the buffer (buf_out: the launch's rows plus one block
+        // stay under 2 GiB of y) and are dropped by the hardware instead of
+        // being tested per store.
+        const uint32_t rstride = (uint32_t)ldy * 4u;            // bytes per row of y
+        const __amdgpu_buffer_rsrc_t yrs = make_rsrc(out, (uint32_t)M * rstride);
+        const uint32_t lane_row = (uint32_t)(4 * gq) * rstride;
+        auto put_y = [&](int n, int mrow, float v) __attribute__((always_inline)) {
+            // mrow: the wave-uniform part of the row (the lane adds 4gq)
+            const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)mrow * rstride));
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g * v), yrs,
+                                                  (int)(lane_row + (uint32_t)n * 4u + row), 0, 0);
         };
 #pragma unroll
         for (int j = 0; j < Q; ++j) {
             const int t = tile0 + w * Q + j;
-            if (t < NT) {
+            const int n = t * 16 + r;
+            if (t < NT && n < N) {
 #pragma unroll
-                for (int i = 0; i < 8; ++i)
-                    put(t, m0 + 16 * (i ^ rb) + 4 * gq, accF[j][i]);
+                for (int i = 0; i < 8; ++i) {
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        put_y(n, m0 + 16 * (i ^ rb) + e, accF[j][i][e]);
+                }
             }
         }
 #pragma unroll
         for (int j = 0; j < RB; ++j) {
             const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
-            if (t < NT) {
+            const int n = t * 16 + r;
+            if (t < NT && n < N) {
 #pragma unroll
                 for (int i = 0; i < RR; ++i)
-                    put(t, m0 + 16 * (rb + i) + 4 * gq, accR[j][i]);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e)
+                        put_y(n, m0 + 16 * (rb + i) + e, accR[j][i][e]);
             }
         }
         return;
     }
+    // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
     float *y = static_cast<float *>(out);
 #pragma unroll
     for (int j = 0; j < Q; ++j) {
@@ -465,7 +552,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
 }
 
 typedef void (*gemm_fn)(const uint8_t *, const uint8_t *, float, const uint16_t *, void *, int, int,
-                        int64_t, int, int, int);
+                        int64_t, int, int, int, int);
 
 #define Q4P_GEMM_ENTRY(T) gemm_kernel<(T) / 4, (T) % 4, false>
 const gemm_fn kGemmTable[kMaxT + 1] = {
@@ -521,10 +608,15 @@ hipError_t launch_gemm_any(const uint8_t *packed_codes, const uint8_t *packed_sc
             // output columns of this chunk: 16 per tile (8 with silu)
             void *o = silu ? static_cast<void *>(static_cast<uint16_t *>(out) + mb * (N / 2) + 8 * tb)
                            : static_cast<void *>(static_cast<float *>(out) + mb * N + 16 * tb);
+            // outputs through buffer stores (32-bit offsets from o) while the
+            // launch's rows plus one block of rows stay under 2 GiB
+            const int64_t row_bytes = silu ? N : N * 4;     // N/2 bf16 or N fp32
+            const int buf_out = (Mc + kBM) * row_bytes <= (int64_t(1) << 31) ? 1 : 0;
             hipLaunchKernelGGL(silu ? kGemmSiluTable[T] : kGemmTable[T], grid, block, 0, stream,
                                packed_codes + tb * KT * kTileCodeBytes,
                                packed_scales + tb * KT * kTileScaleBytes, g, x + mb * K, o,
-                               (int)Mc, (int)Nc, silu ? N / 2 : N, (int)K, (int)KT, (int)NTc);
+                               (int)Mc, (int)Nc, silu ? N / 2 : N, (int)K, (int)KT, (int)NTc,
+                               buf_out);
             const hipError_t e = hipGetLastError();
             if (e != hipSuccess)
                 return e;
