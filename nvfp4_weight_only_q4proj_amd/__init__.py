@@ -4,7 +4,7 @@ Argument marshalling only: every function checks dtypes, devices, shapes and
 contiguity of torch tensors, then calls the entry point of the same name in
 ``libq4proj.so`` on the current HIP stream.  All arithmetic runs in the HIP
 kernels; there is no fallback path.  Importing this module raises if the
-library has not been built (``python -m nvfp4_weight_only_q4proj_amd._build``
+library has not been built (``python nvfp4_weight_only_q4proj_amd/_build.py``
 or ``__graft_entry__.build()``).
 
 The projection computed is
@@ -28,7 +28,7 @@ LIB_PATH = os.path.join(_HERE, "libq4proj.so")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it with "
-                      "`python -m nvfp4_weight_only_q4proj_amd._build` (gfx950 only)")
+                      "`python nvfp4_weight_only_q4proj_amd/_build.py` (gfx950 only)")
 
 _lib = ctypes.CDLL(LIB_PATH)
 

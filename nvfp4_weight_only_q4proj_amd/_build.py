@@ -1,6 +1,8 @@
 """Build libq4proj.so (gfx950 only) in-tree with hipcc.
 
-    python -m nvfp4_weight_only_q4proj_amd._build
+    python nvfp4_weight_only_q4proj_amd/_build.py
+
+(run by path: importing the package needs the library it builds)
 
 Every HIP source is compiled with packed-FP32 instruction selection turned
 off (-Xclang -target-feature -Xclang -packed-fp32-ops); the host pass warns
