@@ -133,6 +133,25 @@ def test_gemv_every_m(M):
         assert_parity(m.codes, m.scales, m.g, x, y)
 
 
+@pytest.mark.parametrize("M", [1, 129, 200, 383])
+def test_gemm_writes_no_row_past_m(M):
+    """y is the first M rows of a larger buffer whose other rows hold a
+    sentinel: the last 128-row block's rows past M are dropped at the end of
+    the output buffer, so the sentinel must survive bit for bit."""
+    m = q4()
+    N, K = 272, 640
+    w = synth.nvfp4_normal_matrix(90 + M, 1, N, K)
+    x = synth.x_bf16(90 + M, 2, M, K)
+    packed = pack(w.codes, w.scales, N, K)
+    big = torch.full((M + 256, N), 12345.0, dtype=torch.float32, device=DEV)
+    note(f"gemm guard rows M={M} N={N} K={K}")
+    m.q4proj_gemm(packed[0], packed[1], w.g, to_dev_x(x), big[:M], M, N, K)
+    torch.cuda.synchronize()
+    tail = big[M:].cpu()
+    assert bool((tail == 12345.0).all()), "rows past M were written"
+    assert_parity(w.codes, w.scales, w.g, x, big[:M].cpu().numpy())
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_nan_and_zero_scales(kind):
     codes, scales, x = pins.tiny_inputs(7, 40, 96, 77)

@@ -68,6 +68,22 @@ def test_every_m(M):
         assert_silu_parity(mat, x, F, h)
 
 
+@pytest.mark.parametrize("M", [1, 130, 255])
+def test_gemm_writes_no_row_past_m(M):
+    """h is the first M rows of a larger buffer filled with a sentinel; the
+    fused GEMM must leave every row past M untouched."""
+    F, K = 136, 512
+    mat = fused_matrix(95 + M, F, K)
+    x = synth.x_bf16(95, M, M, K)
+    packed = pack(mat.codes, mat.scales, 2 * F, K)
+    big = torch.full((M + 256, F), 0x1234, dtype=torch.int16, device=DEV)
+    note(f"gemm_silu_mul guard rows M={M} F={F} K={K}")
+    q4().q4proj_gemm_silu_mul(packed[0], packed[1], mat.g, to_dev_x(x), big[:M], M, F, K)
+    torch.cuda.synchronize()
+    assert bool((big[M:].cpu() == 0x1234).all()), "rows past M were written"
+    assert_silu_parity(mat, x, F, big[:M].cpu().numpy().view(np.uint16))
+
+
 # Many row tiles per wave at short K (tiles complete inside one wave), and one
 # shape with two K ranges.
 WHOLE = [(1, 32768, 128), (3, 49152, 128), (4, 16384, 256), (16, 8192, 384), (2, 24592, 256),
