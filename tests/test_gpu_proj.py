@@ -152,6 +152,22 @@ def test_gemm_writes_no_row_past_m(M):
     assert_parity(w.codes, w.scales, w.g, x, big[:M].cpu().numpy())
 
 
+@pytest.mark.parametrize("M,N,K", [(1, 4099, 640), (7, 4352, 17408), (16, 300, 1040)])
+def test_gemv_writes_nothing_past_y(M, N, K):
+    """y (M x N, ragged N, one and two K ranges) is the start of a larger
+    sentinel-filled buffer: nothing after its M*N elements may change."""
+    m = q4()
+    w = synth.nvfp4_normal_matrix(97 + M, 1, N, K)
+    x = synth.x_bf16(97 + M, 2, M, K)
+    packed = pack(w.codes, w.scales, N, K)
+    big = torch.full((M * N + 4096,), 12345.0, dtype=torch.float32, device=DEV)
+    note(f"gemv guard M={M} N={N} K={K}")
+    m.q4proj_gemv(packed[0], packed[1], w.g, to_dev_x(x), big[:M * N], M, N, K)
+    torch.cuda.synchronize()
+    assert bool((big[M * N:].cpu() == 12345.0).all()), "elements past y were written"
+    assert_parity(w.codes, w.scales, w.g, x, big[:M * N].cpu().numpy().reshape(M, N))
+
+
 @pytest.mark.parametrize("kind", KINDS)
 def test_nan_and_zero_scales(kind):
     codes, scales, x = pins.tiny_inputs(7, 40, 96, 77)
