@@ -206,8 +206,8 @@ def main():
                     help="also run a plain 256 MiB device copy (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path "
-              "(the projection shards by output columns or by k; see DESIGN.md).",
+        print("bench.py measures one GPU only: the projection would shard across GPUs by "
+              "output columns or by k, and no multi-GPU path is implemented.",
               file=sys.stderr)
         sys.exit(2)
 
