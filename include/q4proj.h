@@ -258,14 +258,14 @@ size_t q4proj_quantize_workspace_bytes(int64_t N, int64_t K);
  *      scales  uint8 [N][K/16] e4m3
  *      global_scale  one float in DEVICE memory (copy it to the host once to
  *      pass it by value to the projections).
- * Two-level recipe, each step one IEEE fp32 operation in this order:
- *      amax = max |w|;  g = amax / 2688 (6 * 448; g = 1 when amax == 0)
- *      per 16-element block: t = (amax_b / 6) / g; s = the e4m3 value
- *      nearest to t, ties to the even code, saturating at 448;
- *      inv = 1 / (s * g)
- *      per element: the e2m1 magnitude nearest to |w| * inv, ties to the even
- *      code, saturating at 6; the code's sign bit is w's sign bit; a block
- *      with s * g == 0 gets all-zero codes.
+ * Two-level recipe, every rounding decision exact:
+ *      amax = max |w|;  g = fp32(amax / 2688) (6 * 448; g = 1 when amax == 0)
+ *      per 16-element block (amax_b = its max |w|): s = the e4m3 code
+ *      (0..0x7E) whose value is nearest to the exact quotient
+ *      amax_b / (6 g), ties to the even code (beyond 448: 448);
+ *      per element: the e2m1 magnitude nearest to the exact quotient
+ *      |w| / (e4m3(s) g), ties to the even code (beyond 6: 6); the code's
+ *      sign bit is w's sign bit; a block with s == 0 gets all-zero codes.
  * Deterministic.  The result for non-finite w is unspecified (no fault).
  * Errors: EINVAL (null pointer, N/K <= 0, K % 16 != 0, misaligned w or
  *         codes, overlapping buffers), EWORKSPACE, EDEVICE, EHIP.

@@ -3,14 +3,39 @@
 //
 // The FlashRT "Qwen3.6 NVFP4 usage" page converts a checkpoint to NVFP4 at
 // load time (its MTP checkpoint entry: FP8 -> BF16 -> NVFP4).  Two-level
-// recipe, every rounding decision one IEEE fp32 operation in this order:
-//     amax = max |w|,   g = amax / 2688   (g = 1 when amax == 0)
-//   per 16-element block:
-//     t = (amax_b / 6) / g,   s = e4m3 nearest to t (ties to even, <= 448)
-//     unit = e4m3(s) * g,     inv = 1 / unit
+// recipe:
+//     amax = max |w|,   g = fp32(amax / 2688)   (g = 1 when amax == 0)
+//   per 16-element block, amax_b = max |w| over the block:
+//     s    = the e4m3 code (0..0x7E) whose value is nearest to the exact
+//            quotient amax_b / (6 g), ties to the even code
 //   per element:
-//     r = |w| * inv,   code = e2m1 magnitude nearest to r (ties to the even
-//     code, <= 6; NaN -> 0), bit 3 = sign of w; all codes 0 when unit == 0.
+//     code = the e2m1 magnitude (0..7) nearest to the exact quotient
+//            |w| / (e4m3(s) g), ties to the even code; bit 3 = sign of w;
+//            all codes 0 when s == 0.
+//
+// The decisions are exact, not those of an fp32 evaluation of the quotients:
+//  * scale: an fp32 estimate of the quotient gives a code at most one away
+//    from the nearest; the two midpoints around it are then compared with
+//    amax_b exactly.  A midpoint times 6 has at most 7 significant bits and g
+//    24, so fma(6 mu, g, -amax_b) is the exact difference rounded once, and
+//    its sign (zero included) is the exact comparison.
+//  * codes: each element is converted twice, with 1/(e4m3(s) g) raised and
+//    lowered by 2^-19 (more than the three fp32 roundings of the estimate), by
+//    gfx950's fp32 -> fp4 conversion (nearest even, verified on the device
+//    for every fp32 input).  The exact quotient lies strictly between the two
+//    estimates and the rounding is monotone, so where both give the same
+//    code for an element, that is the exact one.  Where they differ (an
+//    element within ~2^-19 of a midpoint: about 0.2 % of the elements of
+//    ordinary weights, as g = amax / 2688 and bf16 weights put many
+//    quotients within 2^-23 of a midpoint) they are neighbours c, c + 1, and
+//    one comparison with the midpoint between them decides: the midpoint
+//    times e4m3(s) is exact in fp32 (at most 7 bits), and fma(mid * s, g,
+//    -|w|) is again the exact difference rounded once.
+//  * tiny tensors: when g < 2^-100 (or a block's e4m3(s) g < 2^-100) the
+//    differences could fall below the smallest fp32 subnormal and round to
+//    zero; both sides of every comparison are then multiplied by 2^64
+//    (exact) and every element of the block is decided by comparisons with
+//    all seven midpoints.
 //
 // Two launches, both bound by HBM: (1) a grid-stride max of |w| into one slot
 // per workgroup; (2) every workgroup of the quantize launch first reduces
@@ -18,14 +43,6 @@
 // g with no further synchronisation and no scratch state survives the call.
 // A thread owns one 16-element block: 32 B in, 8 B of codes and 1 scale out,
 // consecutive lanes on consecutive blocks (contiguous wave segments).
-//
-// Element rounding uses gfx950's fp32 -> fp4 conversion with scale 1.0 on
-// w * inv (sign kept): checked on the device against the nearest-even rule
-// above for every non-NaN fp32 input (ties, saturation at 6, infinities,
-// negative zero -> code 8 all agree).  It returns a nonzero code for NaN, and
-// w * inv is NaN only for w = 0 with inv = inf (unit below 2^-128), so such
-// blocks take the threshold form instead.  This cuts the loop from ~24 VALU
-// per element to ~3, which is what kept the pass below the HBM rate.
 #include "q4p_device.h"
 #include "q4p_launch.h"
 
@@ -87,8 +104,9 @@ quant_amax_kernel(const uint4 *__restrict__ w, int64_t n16, uint32_t *__restrict
         slots[blockIdx.x] = m;
 }
 
-// e4m3 code nearest to t (0 <= t, finite), ties to the even code, values
-// above 448 saturating to 448 (0x7E)
+// e4m3 code nearest to t (0 <= t, finite, normal or zero), ties to the even
+// code, values above 448 saturating to 448 (0x7E): the estimate that the
+// exact comparisons below correct by at most one code
 __device__ __forceinline__ uint32_t e4m3_nearest(float t)
 {
     if (t > 448.0f)
@@ -109,13 +127,14 @@ __device__ __forceinline__ uint32_t e4m3_nearest(float t)
     return c > 0x7Eu ? 0x7Eu : c;
 }
 
-// e2m1 magnitude code nearest to r (ties to the even code, above 6 -> 6,
-// NaN -> 0): the number of decision points r has passed
-__device__ __forceinline__ uint32_t e2m1_nearest(float r)
+__device__ __forceinline__ float e4m3_value(uint32_t c) { return e4m3_to_f32<0>(c); }
+
+// a / d has passed the midpoint lim / d (d > 0) between codes `upper` - 1 and
+// `upper`: a > lim, or a == lim with `upper` even.  diff = lim - a, rounded
+// once from the exact value (an fma), so its sign is exact.
+__device__ __forceinline__ bool passed(float diff, uint32_t upper)
 {
-    return (uint32_t)(r > 0.25f) + (uint32_t)(r >= 0.75f) + (uint32_t)(r > 1.25f) +
-           (uint32_t)(r >= 1.75f) + (uint32_t)(r > 2.5f) + (uint32_t)(r >= 3.5f) +
-           (uint32_t)(r > 5.0f);
+    return diff < 0.0f || (diff == 0.0f && !(upper & 1u));
 }
 
 // two fp32 -> two e2m1 codes (a low nibble, b high) in byte SEL of old, the
@@ -128,6 +147,35 @@ __device__ __forceinline__ uint32_t fp4_pair(uint32_t old, float a, float b)
 
 __device__ __forceinline__ float bf16_lo(uint32_t v) { return __builtin_bit_cast(float, v << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t v) { return __builtin_bit_cast(float, v & 0xFFFF0000u); }
+
+// the eight element pairs of a block (words wd) -> codes, converting w * inv
+template <typename T>
+__device__ __forceinline__ void fp4_block(const uint32_t (&wd)[8], float inv, T (&out)[2])
+{
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        // elements 2i, 2i+1 -> byte i: low nibble 2i, high nibble 2i+1
+        const float a = bf16_lo(wd[i]) * inv, b2 = bf16_hi(wd[i]) * inv;
+        switch (i & 3) {
+        case 0: out[i >> 2] = fp4_pair<0>(out[i >> 2], a, b2); break;
+        case 1: out[i >> 2] = fp4_pair<1>(out[i >> 2], a, b2); break;
+        case 2: out[i >> 2] = fp4_pair<2>(out[i >> 2], a, b2); break;
+        default: out[i >> 2] = fp4_pair<3>(out[i >> 2], a, b2); break;
+        }
+    }
+}
+
+// exact e2m1 magnitude code of |w| * 2^E / (v_s * g * 2^E): seven
+// comparisons with the midpoints (each mu * v_s exact in fp32)
+__device__ __forceinline__ uint32_t e2m1_exact(float aw, float vs, float gs)
+{
+    const float mu[7] = {0.25f, 0.75f, 1.25f, 1.75f, 2.5f, 3.5f, 5.0f};
+    uint32_t c = 0;
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+        c += passed(__builtin_fmaf(mu[j] * vs, gs, -aw), (uint32_t)j + 1u) ? 1u : 0u;
+    return c;
+}
 
 __global__ void __launch_bounds__(kQuantThreads)
 quant_kernel(const uint4 *__restrict__ w, int64_t nblk, const uint32_t *__restrict__ slots,
@@ -143,38 +191,70 @@ quant_kernel(const uint4 *__restrict__ w, int64_t nblk, const uint32_t *__restri
     const float g = amax == 0.0f ? 1.0f : amax / 2688.0f;
     if (blockIdx.x == 0 && threadIdx.x == 0)
         *gout = g;
+    // comparisons of tiny tensors run on values scaled by 2^64 (exact)
+    const bool tiny = g < 0x1p-100f;
+    const float gs = tiny ? g * 0x1p64f : g;
+    const float escale = tiny ? 0x1p64f : 1.0f;
 
     const int64_t stride = (int64_t)gridDim.x * kQuantThreads;
     for (int64_t b = (int64_t)blockIdx.x * kQuantThreads + threadIdx.x; b < nblk; b += stride) {
         const uint4 v0 = w[2 * b], v1 = w[2 * b + 1];
         const uint32_t wd[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
-        const float amax_b = bf16_lo(max(absmax8(v0), absmax8(v1)));
-        const float t = (amax_b / 6.0f) / g;
-        const uint32_t s = e4m3_nearest(t);
-        const float unit = e4m3_to_f32<0>(s) * g;
-        const float inv = 1.0f / unit;
+        const float as = bf16_lo(max(absmax8(v0), absmax8(v1))) * escale;
+        // scale: the estimate, then the exact test of the midpoints around it
+        uint32_t s = e4m3_nearest((as / 6.0f) / gs);
+        if (s < 0x7Eu && passed(__builtin_fmaf(3.0f * (e4m3_value(s) + e4m3_value(s + 1)), gs, -as),
+                                s + 1))
+            ++s;
+        else if (s > 0u && !passed(__builtin_fmaf(3.0f * (e4m3_value(s - 1) + e4m3_value(s)), gs,
+                                                  -as),
+                                   s))
+            --s;
+        const float vs = e4m3_value(s);
         uint32_t out[2] = {0u, 0u};
-        if (unit != 0.0f && inv != __builtin_inff()) {
+        const float unit = vs * g;
+        if (s != 0u && !tiny && unit >= 0x1p-100f) {
+            const float inv = 1.0f / unit;
+            uint32_t hi[2] = {0u, 0u};
+            fp4_block(wd, inv * (1.0f + 0x1p-19f), hi);
+            fp4_block(wd, inv * (1.0f - 0x1p-19f), out);
+            // elements whose two estimates differ lie within ~2^-19 of the
+            // midpoint between magnitudes c (out) and c + 1 (hi): decide each
+            // by one exact comparison with that midpoint
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                // elements 2i, 2i+1 -> byte i: low nibble 2i, high nibble 2i+1
-                const float a = bf16_lo(wd[i]) * inv, b2 = bf16_hi(wd[i]) * inv;
-                switch (i & 3) {
-                case 0: out[i >> 2] = fp4_pair<0>(out[i >> 2], a, b2); break;
-                case 1: out[i >> 2] = fp4_pair<1>(out[i >> 2], a, b2); break;
-                case 2: out[i >> 2] = fp4_pair<2>(out[i >> 2], a, b2); break;
-                default: out[i >> 2] = fp4_pair<3>(out[i >> 2], a, b2); break;
+            for (int h = 0; h < 2; ++h) {
+                uint32_t d = hi[h] ^ out[h];
+                while (d != 0u) {
+                    const uint32_t sh = (uint32_t)__builtin_ctz(d) & ~3u;   // nibble of the element
+                    const uint32_t e = sh >> 2;                             // element 8h + e
+                    const uint32_t q = e >> 1;
+                    const uint32_t word = q == 0 ? wd[4 * h] : q == 1 ? wd[4 * h + 1]
+                                        : q == 2 ? wd[4 * h + 2] : wd[4 * h + 3];
+                    const float aw = __builtin_fabsf((e & 1u) ? bf16_hi(word) : bf16_lo(word));
+                    const uint32_t nib = (out[h] >> sh) & 15u;
+                    const uint32_t c = nib & 7u;
+                    // the two magnitudes c, c + 1 decoded as one byte
+                    const floatx2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(
+                        c | ((c + 1u) << 4), 1.0f, 0);
+                    const float mu = 0.5f * (v2[0] + v2[1]);
+                    const uint32_t cx =
+                        c + (passed(__builtin_fmaf(mu * vs, g, -aw), c + 1u) ? 1u : 0u);
+                    out[h] = (out[h] & ~(15u << sh)) | (((nib & 8u) | cx) << sh);
+                    d &= ~(15u << sh);
                 }
             }
-        } else if (unit != 0.0f) {
+        } else if (s != 0u) {
+            // tiny scales: every element by the exact comparisons
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                // elements 2i (low half) and 2i+1 (high half) -> one byte
-                const uint32_t qlo = e2m1_nearest(__builtin_fabsf(bf16_lo(wd[i])) * inv) |
-                                     ((wd[i] >> 12) & 8u);
-                const uint32_t qhi = e2m1_nearest(__builtin_fabsf(bf16_hi(wd[i])) * inv) |
-                                     ((wd[i] >> 28) & 8u);
-                out[i >> 2] |= (qlo | (qhi << 4)) << (8 * (i & 3));
+                const uint32_t qlo =
+                    e2m1_exact(__builtin_fabsf(bf16_lo(wd[i])) * escale, vs, gs) |
+                    ((wd[i] >> 12) & 8u);
+                const uint32_t qhi =
+                    e2m1_exact(__builtin_fabsf(bf16_hi(wd[i])) * escale, vs, gs) |
+                    ((wd[i] >> 28) & 8u);
+                const uint32_t byte = (qlo | (qhi << 4)) << (8 * (i & 3));
+                out[i >> 2] = (i & 3) ? (out[i >> 2] | byte) : byte;
             }
         }
         codes[b] = make_uint2(out[0], out[1]);

@@ -4,8 +4,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
 ``bench.py`` may import this package.  The HIP library never touches it and it
 never touches the HIP library: the two share no code.
 
-The arithmetic lives in ``oracle.c`` (plain C, fp64).  This module builds it
-with gcc into ``liboracle.so`` and exposes numpy-level wrappers:
+The arithmetic lives in ``oracle.c`` (plain C, fp64).  ``__graft_entry__.build()``
+compiles it with gcc into ``liboracle.so`` (this module never compiles
+anything itself: it is loaded by processes that already use the GPU, which
+must not start other programs); the module exposes numpy-level wrappers:
 
 * :func:`e2m1`, :func:`e4m3`, :func:`bf16` — element decoders (closed forms),
 * :func:`dequant_row` — one weight row in fp64,
@@ -14,7 +16,8 @@ with gcc into ``liboracle.so`` and exposes numpy-level wrappers:
 * :func:`argmax_check` — the acceptance test of a greedy argmax (index and
   value) over logits rows,
 * :func:`quantize` / :func:`quant_global_scale` — the NVFP4 quantizer
-  (bf16 weights -> codes, e4m3 block scales, global scale), decisions in fp32,
+  (bf16 weights -> codes, e4m3 block scales, global scale), every rounding
+  decision taken exactly (nearest value to the exact quotient, ties to even),
 * :func:`silu_mul_cols` / :func:`check_bf16` — the fused gate/up projection
   h = silu(gate) * up on a weight whose gate and up rows are interleaved in
   groups of 8, its error allowance, and the bf16 acceptance test.
@@ -50,12 +53,13 @@ _lib = None
 
 
 def load(path: str = LIB):
-    """Load (building first if absent) and type the oracle library."""
+    """Load and type the oracle library (built by ``build()``)."""
     global _lib
     if path == LIB and _lib is not None:
         return _lib
     if not os.path.exists(path):
-        build(out=path)
+        raise ImportError(f"{path} is missing: run `python __graft_entry__.py build` "
+                          "(or oracle.build()) before loading the oracle")
     lib = ctypes.CDLL(path)
     i64, dbl, vp = ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
     lib.orc_e2m1.argtypes = [ctypes.c_uint]
@@ -81,10 +85,10 @@ def load(path: str = LIB):
     lib.orc_check_bf16.restype = i64
     lib.orc_argmax_check.argtypes = [i64, i64, vp, vp, dbl, vp, vp]
     lib.orc_argmax_check.restype = i64
-    lib.orc_quant_e4m3.argtypes = [ctypes.c_float]
-    lib.orc_quant_e4m3.restype = ctypes.c_uint
-    lib.orc_quant_e2m1.argtypes = [ctypes.c_float]
-    lib.orc_quant_e2m1.restype = ctypes.c_uint
+    lib.orc_quant_scale.argtypes = [ctypes.c_float, ctypes.c_float]
+    lib.orc_quant_scale.restype = ctypes.c_uint
+    lib.orc_quant_code.argtypes = [ctypes.c_float, ctypes.c_uint, ctypes.c_float]
+    lib.orc_quant_code.restype = ctypes.c_uint
     lib.orc_quant_global_scale.argtypes = [i64, vp]
     lib.orc_quant_global_scale.restype = ctypes.c_float
     lib.orc_quantize.argtypes = [i64, i64, vp, ctypes.c_float, vp, vp]
@@ -99,7 +103,12 @@ def _ptr(a: np.ndarray) -> int:
 
 
 def default_threads() -> int:
-    return max(1, min(os.cpu_count() or 1, 16))
+    """The CPU cores this process may run on (its affinity set), which on a
+    shared host can be fewer than os.cpu_count()."""
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except (AttributeError, OSError):
+        return max(1, os.cpu_count() or 1)
 
 
 def e2m1(code: int, lib=None) -> float:

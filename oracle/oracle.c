@@ -333,67 +333,72 @@ int64_t orc_check_bf16(int64_t count, const double *href, const double *bound,
  * NVFP4 recipe: a per-tensor fp32 global scale that maps the tensor's largest
  * magnitude to the largest representable product 6 * 448, an e4m3 scale per
  * 16 consecutive k that maps the block's largest magnitude to the largest
- * e2m1 magnitude 6, and each element rounded to the nearest e2m1 value.
+ * e2m1 magnitude 6, and each element rounded to the nearest e2m1 value:
  *
- * The rounding decisions are taken in fp32 with IEEE round-to-nearest
- * operations, in this order (the kernel's precision, so both sides decide
- * alike):
  *     amax = max |w|                       (exact; bf16 values)
- *     g    = amax / 2688                    (g = 1 when amax == 0)
- *   per 16-element block b:
- *     t    = (amax_b / 6) / g
- *     s_b  = the e4m3 code nearest to t, ties to the even code, t beyond
- *            448 saturating to 448 (code 0x7E)
- *     unit = e4m3(s_b) * g,   inv = 1 / unit
- *   per element:
- *     r    = |w| * inv
- *     code = the e2m1 magnitude code nearest to r, ties to the even code,
- *            r beyond 6 saturating to 6 (code 7), NaN (0 * inf) giving 0;
- *            bit 3 = the sign bit of w
- *   and every code of a block is 0 when unit == 0.
- * "Nearest" is found by searching the decoded code values (orc_e2m1,
- * orc_e4m3) in fp64, where the distances are exact.
+ *     g    = fp32(amax / 2688)             (one IEEE division; 1 when amax == 0)
+ *   per 16-element block b, with amax_b = max over the block of |w|:
+ *     s_b  = the e4m3 code in 0..0x7E whose value is nearest to the exact
+ *            quotient amax_b / (6 g), ties to the even code (a quotient past
+ *            448 therefore gets 448, code 0x7E)
+ *   per element, with unit = e4m3(s_b) * g (exact real product):
+ *     code = the e2m1 magnitude code in 0..7 whose value is nearest to the
+ *            exact quotient |w| / unit, ties to the even code (past 6: 6);
+ *            bit 3 = the sign bit of w (so small negatives give code 8, -0)
+ *   and every code of a block is 0 when unit == 0 (scale code 0).
+ *
+ * The quotients are never formed.  The code values v_0 < v_1 < ... are
+ * increasing in code order, so the nearest value is found by walking the
+ * midpoints (v_c + v_{c+1}) / 2 upward while the quotient lies above them
+ * (at a quotient equal to a midpoint: to the even one of c, c+1).  Comparing
+ * a / d with a midpoint mu, d > 0, is comparing a with d * mu, and both
+ * products below are exact in fp64: 6 * g * mu has at most 2 + 24 + 5 = 31
+ * significant bits (g is an fp32 value, an e4m3 midpoint has at most 5) and
+ * e4m3(s) * g * mu at most 4 + 24 + 3 = 31 (an e2m1 midpoint has at most 3),
+ * far inside fp64's 53 bits and its exponent range, while a (a bf16 value)
+ * is exact in fp64 too.  So every decision is exact: no rounding step of the
+ * kernel's arithmetic takes part in what the result is.
  */
 
-/* nearest e4m3 code in 0..0x7E to t >= 0 (ties to the even code) */
-static unsigned quant_e4m3(float t)
+/* e4m3 code (0..0x7E) nearest to a / (6 g), a >= 0, g > 0, ties to the even code */
+static unsigned quant_scale(double a, double g)
 {
-    if (t > 448.0f)
-        return 0x7Eu;
-    unsigned best = 0;
-    double bd = INFINITY;
-    for (unsigned c = 0; c <= 0x7Eu; ++c) {
-        const double d = fabs((double)t - orc_e4m3(c));
-        if (d < bd || (d == bd && (c & 1u) == 0)) {
-            best = c;
-            bd = d;
-        }
+    unsigned c = 0;
+    while (c < 0x7Eu) {
+        const double lim = 6.0 * g * ((orc_e4m3(c) + orc_e4m3(c + 1)) / 2.0);
+        if (a > lim || (a == lim && ((c + 1) & 1u) == 0))
+            ++c;
+        else
+            break;
     }
-    return best;
+    return c;
 }
 
-/* nearest e2m1 magnitude code in 0..7 to r >= 0 (ties to the even code) */
-static unsigned quant_e2m1(float r)
+/* e2m1 magnitude code (0..7) nearest to a / unit, a >= 0, unit > 0, ties to
+ * the even code */
+static unsigned quant_code(double a, double unit)
 {
-    if (isnan(r))
-        return 0u;
-    if (r > 6.0f)
-        return 7u;
-    unsigned best = 0;
-    double bd = INFINITY;
-    for (unsigned c = 0; c <= 7u; ++c) {
-        const double d = fabs((double)r - orc_e2m1(c));
-        if (d < bd || (d == bd && (c & 1u) == 0)) {
-            best = c;
-            bd = d;
-        }
+    unsigned c = 0;
+    while (c < 7u) {
+        const double lim = unit * ((orc_e2m1(c) + orc_e2m1(c + 1)) / 2.0);
+        if (a > lim || (a == lim && ((c + 1) & 1u) == 0))
+            ++c;
+        else
+            break;
     }
-    return best;
+    return c;
 }
 
-/* single-value forms of the two rounding steps (for the tests) */
-unsigned orc_quant_e4m3(float t) { return quant_e4m3(t); }
-unsigned orc_quant_e2m1(float r) { return quant_e2m1(r); }
+/* single-value forms of the two rounding steps (for the tests):
+ * the scale code for a block maximum amax_b under global scale g, and the
+ * magnitude code of |w| = a under scale code s and global scale g */
+unsigned orc_quant_scale(float amax_b, float g) { return quant_scale((double)amax_b, (double)g); }
+
+unsigned orc_quant_code(float a, unsigned s, float g)
+{
+    const double unit = orc_e4m3(s) * (double)g;
+    return unit == 0.0 ? 0u : quant_code((double)a, unit);
+}
 
 static float bf16_to_float(uint16_t b)
 {
@@ -423,23 +428,21 @@ void orc_quantize(int64_t N, int64_t K, const uint16_t *w, float g, uint8_t *cod
     for (int64_t n = 0; n < N; ++n) {
         for (int64_t b = 0; b < K / 16; ++b) {
             const uint16_t *wb = w + n * K + 16 * b;
-            float amax_b = 0.0f;
+            double amax_b = 0.0;
             for (int i = 0; i < 16; ++i) {
-                const float a = fabsf(bf16_to_float(wb[i]));
+                const double a = fabs((double)bf16_to_float(wb[i]));
                 if (a > amax_b)
                     amax_b = a;
             }
-            const float t = (amax_b / 6.0f) / g;
-            const unsigned s = quant_e4m3(t);
-            const float unit = (float)orc_e4m3(s) * g;
-            const float inv = 1.0f / unit;
+            const unsigned s = quant_scale(amax_b, (double)g);
+            const double unit = orc_e4m3(s) * (double)g;
             scales[n * (K / 16) + b] = (uint8_t)s;
             for (int i = 0; i < 16; i += 2) {
                 unsigned q[2];
                 for (int j = 0; j < 2; ++j) {
                     const uint16_t bits = wb[i + j];
-                    const float r = fabsf(bf16_to_float(bits)) * inv;
-                    q[j] = unit == 0.0f ? 0u : quant_e2m1(r) | ((bits >> 15) << 3);
+                    const double a = fabs((double)bf16_to_float(bits));
+                    q[j] = unit == 0.0 ? 0u : quant_code(a, unit) | ((bits >> 15) << 3);
                 }
                 codes[n * (K / 2) + 8 * b + i / 2] = (uint8_t)(q[0] | (q[1] << 4));
             }

@@ -52,11 +52,15 @@ _lib = None
 
 
 def load():
+    """Load and type the generator library (built by ``build()``; this module
+    never compiles anything itself, since GPU processes load it and must not
+    start other programs)."""
     global _lib
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB):
-        build()
+        raise ImportError(f"{LIB} is missing: run `python __graft_entry__.py build` "
+                          "(or synth.build()) first")
     lib = ctypes.CDLL(LIB)
     u64, i64, dbl, vp = ctypes.c_uint64, ctypes.c_int64, ctypes.c_double, ctypes.c_void_p
     lib.syn_u64.argtypes = [u64, u64, u64]

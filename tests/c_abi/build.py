@@ -4,8 +4,8 @@ shared library with one entry point, abi_consumer_run().
 It links the product library (libq4proj.so), the CPU oracle and the seeded
 input generators, plus the HIP runtime for its own device allocations, with
 run paths relative to the binary so the tree can move.  Test infrastructure:
-called by __graft_entry__.build() and, when the binary is missing, by the
-test that runs it.
+called by __graft_entry__.build() only (the GPU test that runs the consumer
+requires it to be built already).
 """
 from __future__ import annotations
 

@@ -15,6 +15,7 @@ dropped term, a transposed operand) fails at least one of them —
 """
 from __future__ import annotations
 
+import bisect
 import math
 import os
 from fractions import Fraction
@@ -434,37 +435,171 @@ def golden_e2m1_rounding():
 
 
 def pin_quant_e2m1_rounding(lib):
-    """e2m1 rounding against the OCP MX conversion rule, tabulated."""
+    """e2m1 rounding against the OCP MX conversion rule, tabulated: the code of
+    |w| = v under scale 1.0 (0x38) and g = 1, and the same under scale 0.5
+    (0x30) and g = 2^-7 for |w| = v * 2^-8 (exact); saturation past 6."""
     rows = golden_e2m1_rounding()
     assert len(rows) >= 20
     for v, c in rows:
-        assert lib.orc_quant_e2m1(v) == c, (v, c, lib.orc_quant_e2m1(v))
-    assert lib.orc_quant_e2m1(float("inf")) == 7
+        assert lib.orc_quant_code(v, 0x38, 1.0) == c, (v, c, lib.orc_quant_code(v, 0x38, 1.0))
+        if v < 1e29:
+            assert np.float32(v * 2.0 ** -8) * np.float32(2.0 ** 8) == np.float32(v)
+            assert lib.orc_quant_code(v * 2.0 ** -8, 0x30, 2.0 ** -7) == c, v
+    assert lib.orc_quant_code(float("inf"), 0x38, 1.0) == 7
+    assert lib.orc_quant_code(1.0, 0x00, 1.0) == 0            # scale 0: code 0
+
+
+def _f32_22(v):
+    """v rounded to 22 significant bits (so that 0.375 v stays exact in fp32)"""
+    v = np.asarray(v, np.float64)
+    m, e = np.frexp(v)
+    return np.ldexp(np.round(m * 2.0 ** 22) / 2.0 ** 22, e).astype(np.float32)
 
 
 def pin_quant_e4m3_torch(lib):
-    """e4m3 rounding against torch's float8_e4m3fn cast (round to nearest
-    even) on every value, every midpoint between neighbours, one fp32 ulp to
-    each side of every midpoint, and random values in [0, 448]; saturation
-    above 448 in closed form."""
+    """e4m3 scale rounding against torch's float8_e4m3fn cast (round to nearest
+    even) of t = amax_b / (6 g), with g a power of two so that amax_b = 6 g t
+    is exact: every value, every midpoint between neighbours, the 22-bit
+    neighbours of every midpoint, random values in [0, 448] and below 2^-6;
+    saturation above 448 in closed form."""
     vals = pins_e4m3_positive()
     mids = ((vals[:-1].astype(np.float64) + vals[1:]) / 2).astype(np.float32)
     assert np.array_equal(mids.astype(np.float64), (vals[:-1].astype(np.float64) + vals[1:]) / 2)
     rng = np.random.default_rng(9)
-    t = np.concatenate([vals, mids, np.nextafter(mids, np.float32(0)),
-                        np.nextafter(mids, np.float32(np.inf)),
-                        rng.uniform(0, 448, 3000).astype(np.float32),
-                        (2.0 ** rng.uniform(-12, -5, 1000)).astype(np.float32)])
+    up = _f32_22(mids.astype(np.float64) * (1 + 2.0 ** -21))
+    dn = _f32_22(mids.astype(np.float64) * (1 - 2.0 ** -21))
+    assert (up > mids).all() and (dn < mids).all()
+    t = np.concatenate([vals, mids, up, dn, _f32_22(rng.uniform(0, 448, 3000)),
+                        _f32_22(2.0 ** rng.uniform(-12, -5, 1000))])
     want = torch.from_numpy(t).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
-    got = np.array([lib.orc_quant_e4m3(float(v)) for v in t])
-    assert np.array_equal(got, want), t[got != want][:5]
+    for g in (2.0 ** -4, 2.0 ** -20, 2.0 ** 3):
+        a = t.astype(np.float64) * 6.0 * g
+        assert np.array_equal(a.astype(np.float32).astype(np.float64), a)
+        got = np.array([lib.orc_quant_scale(float(v), g) for v in a])
+        assert np.array_equal(got, want), (g, t[got != want][:5])
     for v in (448.0001, 460.0, 464.0, 1e6, float("inf")):
-        assert lib.orc_quant_e4m3(v) == 0x7E
+        assert lib.orc_quant_scale(v * 6 * 2.0 ** -4, 2.0 ** -4) == 0x7E
 
 
 def pins_e4m3_positive():
     """The 127 non-negative finite e4m3 values in code order (torch's decoder)."""
     return torch.arange(0, 0x7F, dtype=torch.uint8).view(torch.float8_e4m3fn).float().numpy()
+
+
+# exact rational reference of the quantiser's two rounding steps: the grid
+# value nearest to a rational quotient, ties to the even code, found with
+# fractions.Fraction (every float is an exact rational)
+
+def _fr_grids():
+    e4 = [Fraction(float(v)) for v in pins_e4m3_positive()]
+    table = golden_e2m1()
+    e2 = [Fraction(table[c]) for c in range(8)]
+    return e4, e2
+
+
+def _fr_nearest(q, grid):
+    i = bisect.bisect_left(grid, q)
+    if i == 0:
+        return 0
+    if i == len(grid):
+        return len(grid) - 1
+    dl, du = q - grid[i - 1], grid[i] - q
+    if dl < du:
+        return i - 1
+    if du < dl:
+        return i
+    return i - 1 if (i - 1) % 2 == 0 else i
+
+
+def fr_quant_scale(a, g, e4):
+    return _fr_nearest(Fraction(a) / (6 * Fraction(g)), e4)
+
+
+def fr_quant_code(a, s, g, e4, e2):
+    if s == 0:
+        return 0
+    return _fr_nearest(Fraction(a) / (e4[s] * Fraction(g)), e2)
+
+
+def fr_quantize(bits, N, K):
+    """The quantiser's definition in exact rationals: g = fp32(amax / 2688)
+    (numpy's IEEE fp32 division), then per block the nearest e4m3 scale and per
+    element the nearest e2m1 magnitude with w's sign bit."""
+    e4, e2 = _fr_grids()
+    wv = pins_bf16_of(np.ascontiguousarray(bits, np.uint16).ravel()).reshape(N, K)
+    amax = np.abs(wv).max()
+    g = 1.0 if amax == 0 else float(np.float32(amax) / np.float32(2688.0))
+    codes = np.zeros((N, K // 2), np.uint8)
+    scales = np.zeros((N, K // 16), np.uint8)
+    sign = (np.ascontiguousarray(bits, np.uint16).reshape(N, K) >> 15).astype(np.uint8)
+    for n in range(N):
+        for b in range(K // 16):
+            blk = np.abs(wv[n, 16 * b:16 * b + 16])
+            s = fr_quant_scale(float(blk.max()), g, e4)
+            scales[n, b] = s
+            q = [fr_quant_code(float(a), s, g, e4, e2) | (int(sign[n, 16 * b + i]) << 3 if s else 0)
+                 for i, a in enumerate(blk)]
+            codes[n, 8 * b:8 * b + 8] = [q[2 * i] | (q[2 * i + 1] << 4) for i in range(8)]
+    return codes, scales, g
+
+
+def pin_quant_fraction(lib):
+    """orc_quant_scale / orc_quant_code against the exact rational reference on
+    random values under random fp32 global scales (normal, subnormal and
+    large), and on quotients constructed within one fp32 step of every
+    midpoint: a = bf16 w with g = fp32(w / (mid * v)) and its fp32 neighbours,
+    where fp32 evaluations of the quotient decide wrongly."""
+    e4, e2 = _fr_grids()
+    rng = np.random.default_rng(13)
+    gs = np.concatenate([np.float32(2.0 ** rng.uniform(-30, -5, 24)),
+                         np.float32(2.0 ** rng.uniform(-148, -127, 4)),
+                         np.float32(2.0 ** rng.uniform(5, 30, 4))]).astype(np.float64)
+    for g in gs:
+        a = (np.abs(rng.normal(0, 1, 40)) * 2688 * g / 3).astype(np.float32).astype(np.float64)
+        for v in a:
+            assert lib.orc_quant_scale(v, g) == fr_quant_scale(v, g, e4), (v, g)
+            s = int(rng.integers(0, 0x7F))
+            assert lib.orc_quant_code(v, s, g) == fr_quant_code(v, s, g, e4, e2), (v, s, g)
+    w = pins_bf16_of(rng.integers(0x3C00, 0x3F00, 120).astype(np.uint16))    # bf16 in [2^-7, 0.5)
+    mids_e2 = [(e2[i] + e2[i + 1]) / 2 for i in range(7)]
+    mids_e4 = [(e4[i] + e4[i + 1]) / 2 for i in range(0x7E)]
+    near = 0
+    for k, v in enumerate(w):
+        s = int(rng.integers(1, 0x7F))
+        mu = mids_e2[k % 7]
+        g0 = np.float32(v / float(mu * e4[s]))
+        for g in (np.nextafter(g0, np.float32(0)), g0, np.nextafter(g0, np.float32(1))):
+            g = float(g)
+            want = fr_quant_code(v, s, g, e4, e2)
+            assert lib.orc_quant_code(v, s, g) == want, (v, s, g)
+            # the quotient evaluated in fp32 (1 / (s g), then times |w|) on the
+            # other side of the midpoint than the exact one
+            exact = Fraction(v) / (e4[s] * Fraction(g))
+            r32 = Fraction(float(np.float32(v) * (np.float32(1) / (np.float32(float(e4[s]))
+                                                                   * np.float32(g)))))
+            near += int((r32 > mu) != (exact > mu) or (r32 == mu) != (exact == mu))
+        m = mids_e4[(7 * k) % 0x7E]
+        g0 = np.float32(v / float(6 * m))
+        for g in (np.nextafter(g0, np.float32(0)), g0, np.nextafter(g0, np.float32(1))):
+            g = float(g)
+            assert lib.orc_quant_scale(v, g) == fr_quant_scale(v, g, e4), (v, g)
+    assert near > 0          # the construction does reach quotients fp32 misplaces
+
+
+def pin_quantize_fraction(lib):
+    """orc_quantize against the exact rational definition (fr_quantize) on the
+    tensors built at and next to the rounding ties (tests/quant_inputs.py):
+    g = 2^-7 with exact ties (ties to the even code), and a g of 24
+    significant bits with hundreds of elements within 2^-23 of a tie."""
+    import quant_inputs
+    for kind in ("pow2", "near"):
+        bits, _ = quant_inputs.tie_weights(kind, K=256)
+        N, K = bits.shape
+        codes, scales, g = oracle.quantize(bits, N, K, lib=lib)
+        rc, rs, rg = fr_quantize(bits, N, K)
+        assert g == rg, (kind, g, rg)
+        assert np.array_equal(scales, rs), (kind, np.argwhere(scales != rs)[:5])
+        assert np.array_equal(codes, rc), (kind, np.argwhere(codes != rc)[:5])
 
 
 def pin_quant_global_scale(lib):
@@ -506,20 +641,11 @@ def pins_bf16_of(bits):
     return torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
 
 
-def _nearest_ok(x, grid, chosen, rel=2.0 ** -20):
-    """chosen is the grid value nearest to x, or x lies within rel of the
-    midpoint between chosen and the nearest value (fp32 decisions on x)."""
-    d = np.abs(grid[None, :] - x[:, None])
-    best = d.min(axis=1)
-    dc = np.abs(chosen - x)
-    return (dc <= best) | (np.abs(dc - best) <= rel * np.maximum(np.abs(x), 1e-300))
-
-
 def pin_quantize_nearest(lib):
-    """Every scale is the e4m3 value nearest to (amax_b / 6) / g and every
-    code the e2m1 magnitude nearest to |w| / (s g) (beyond 6: 6), with the
-    sign of w, checked in fp64; zero blocks give scale 0 and codes 0; tiny
-    blocks give subnormal or zero scales."""
+    """orc_quantize against the exact rational definition on random N(0, 0.02)
+    weights with zero blocks, blocks small enough for subnormal and zero
+    e4m3 scales, negative zeros and one large element setting g: every
+    scale and code exactly, zero blocks giving scale 0 and codes 0."""
     rng = np.random.default_rng(12)
     N, K = 24, 512
     w = rng.normal(0, 0.02, (N, K))
@@ -530,28 +656,14 @@ def pin_quantize_nearest(lib):
     w[5, 7] = 0.9                                  # the tensor's amax
     w[6, ::3] = -0.0
     bits = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
-    wv = pins_bf16_of(bits).reshape(N, K)
     codes, scales, g = oracle.quantize(bits, N, K, lib=lib)
-    e4 = pins_e4m3_positive().astype(np.float64)
-    e2 = np.array([lib.orc_e2m1(c) for c in range(8)])
-    amax_b = np.abs(wv).reshape(N, K // 16, 16).max(axis=2)
-    t = (amax_b / 6.0 / g).ravel()
-    sv = e4[scales.ravel()]
-    assert _nearest_ok(np.minimum(t, 448.0), e4, sv).all()
+    rc, rs, rg = fr_quantize(bits, N, K)
+    assert g == rg
+    assert np.array_equal(scales, rs), np.argwhere(scales != rs)[:5]
+    assert np.array_equal(codes, rc), np.argwhere(codes != rc)[:5]
     assert (scales[2] == 0).all() and (scales[3, :4] == 0).all()
     assert (scales[4] < 0x08).any() and (scales[4] == 0).any()
-    q = np.empty((N, K), np.uint8)
-    q[:, 0::2] = codes & 15
-    q[:, 1::2] = codes >> 4
-    unit = np.repeat(e4[scales].astype(np.float64) * g, 16, axis=1)
-    live = unit > 0
-    r = np.where(live, np.abs(wv) / np.where(live, unit, 1.0), 0.0)
-    mag = e2[q & 7]
-    ok = _nearest_ok(np.minimum(r[live], 6.0), e2, mag[live])
-    assert ok.all(), np.argwhere(~ok)[:5]
-    assert (q[~live] == 0).all()
-    neg = (bits.reshape(N, K) >> 15) == 1
-    assert ((q[live] >> 3) == neg[live]).all()
+    assert (codes[2] == 0).all()
 
 
 ALL_PINS = [pin_e2m1_table, pin_e4m3_torch, pin_e4m3_landmarks, pin_bf16_torch,
@@ -559,4 +671,5 @@ ALL_PINS = [pin_e2m1_table, pin_e4m3_torch, pin_e4m3_landmarks, pin_bf16_torch,
             pin_invariants, pin_nan_scale, pin_check, pin_silu_mul_torch,
             pin_silu_mul_fused_rows, pin_silu_mul_bound, pin_quant_e2m1_rounding,
             pin_quant_e4m3_torch, pin_quant_global_scale, pin_quantize_exact_recovery,
-            pin_quantize_nearest, pin_argmax_check]
+            pin_argmax_check, pin_quant_fraction, pin_quantize_nearest,
+            pin_quantize_fraction]

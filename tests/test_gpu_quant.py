@@ -1,10 +1,15 @@
 """q4proj_quantize (bf16 -> NVFP4 codes, e4m3 block scales, global scale)
-against the CPU oracle, bit for bit: every rounding decision is specified as
-fp32 IEEE operations on both sides.
+against the CPU oracle, bit for bit.  Every rounding decision is the nearest
+value to an exact quotient (ties to the even code); the oracle takes it in
+exact fp64 comparisons (pinned to exact rationals), the kernel by an fp32
+estimate bracketed and corrected with exact fma comparisons.
 
 * random N(0, 0.02) weights on small and ragged shapes (every element);
 * special tensors: all zero, negative zeros, zero and tiny blocks, bf16
   subnormals and extremes, exact e2m1 and e4m3 rounding ties;
+* every element and scale tie of every scale code, exactly on the tie
+  (g = 2^-7) and within 2^-23 of it (a g of 24 significant bits), one bf16
+  step either side, in blocks of their own;
 * the fused gate/up shape (34816 x 5120) on sampled rows, g over the whole
   tensor;
 * quantize -> pack -> gemv on the GPU against the oracle projection of the
@@ -15,6 +20,7 @@ import pytest
 import torch
 
 import oracle
+import quant_inputs
 import synth
 from gpu_util import DEV, assert_parity, note, pack, project, q4
 
@@ -114,6 +120,14 @@ def test_rounding_ties():
     N = w.shape[0]
     c, s, gq = assert_same(bits, N, 16)
     assert gq == g
+
+
+@pytest.mark.parametrize("kind", ["pow2", "near"])
+def test_tie_tensors(kind):
+    bits, amax = quant_inputs.tie_weights(kind)
+    N, K = bits.shape
+    c, s, g = assert_same(bits, N, K)
+    assert g == np.float32(amax) / np.float32(2688)
 
 
 def test_fused_gate_up_shape_sampled_rows():
