@@ -126,15 +126,12 @@ __device__ __forceinline__ void gemv_half(const uint4 &cw, const uint2 &sw, XA &
         const short4_t bq = __builtin_bit_cast(short4_t, make_uint2(lo, hi));
         p[bb] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, bq, zero, 0, 0, 0);
     }
+    // the block scales, two per conversion (OCP e4m3 on gfx950)
+    const floatx2_t s01 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sv, false);
+    const floatx2_t s23 = __builtin_amdgcn_cvt_pk_f32_fp8((int)sv, true);
 #pragma unroll
     for (int bb = 0; bb < 4; ++bb) {
-        float s;
-        switch (bb) {
-        case 0: s = e4m3_to_f32<0>(sv); break;
-        case 1: s = e4m3_to_f32<1>(sv); break;
-        case 2: s = e4m3_to_f32<2>(sv); break;
-        default: s = e4m3_to_f32<3>(sv); break;
-        }
+        const float s = bb == 0 ? s01[0] : bb == 1 ? s01[1] : bb == 2 ? s23[0] : s23[1];
 #pragma unroll
         for (int i = 0; i < ROWS; ++i)
             acc[i] = __builtin_fmaf(s, p[bb][i], acc[i]);
@@ -588,23 +585,33 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             xs[i] = *reinterpret_cast<const uint4 *>(x + (int64_t)srow[i] * K + k);
     }
 
-    // 2. weight ring prologue, in slot order.  The ring's loads are buffer
-    //    loads: one past the wave's last unit gets a descriptor of size 0,
-    //    which returns zeros without a memory access, so the loads stay
-    //    unconditional and no wave waits at the finish for data it never
-    //    uses.
+    // 2. weight ring prologue, in slot order.
+    //    One K range: the wave's units are contiguous in the packed buffers,
+    //    so each wave gets descriptors sized to its own units; a load past its
+    //    last unit falls outside and returns zeros without a memory access,
+    //    and the ring needs no per-load bookkeeping (position p reads code
+    //    offset 1024p and scale offset 128p).
+    //    K ranges: a unit's packed index is t*KTG + c0 + c for (row tile t,
+    //    range-local k-tile c), walked incrementally, with loads past the
+    //    wave's last unit on a descriptor of size 0.
     const uint32_t cbytes = (uint32_t)((int64_t)a.NT * KTG * 1024);
     const uint32_t sbytes = (uint32_t)((int64_t)a.NT * KTG * 128);
     uint4 cw[PF];
     uint2 sw[PF];
+    const auto rc_w = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint4 *>(pcodes + (int64_t)(KR ? 0 : u0) * 64), 0, (int)(KR ? 0u : (uint32_t)n * 1024u), 0x00020000);
+    const auto rs_w = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint2 *>(pscales + (int64_t)(KR ? 0 : u0) * 16), 0, (int)(KR ? 0u : (uint32_t)n * 128u), 0x00020000);
+    auto load_pos = [&](int s, int pos) {
+        const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(rc_w, lane * 16, pos * 1024, 2 /* non-temporal */);
+        cw[s] = make_uint4(c.x, c.y, c.z, c.w);
+        const u32x2_t v = __builtin_amdgcn_raw_buffer_load_b64(rs_w, r * 8, pos * 128, 0);
+        sw[s] = make_uint2(v.x, v.y);
+    };
     int ld_q = 0;                              // loads issued by this wave
-    // next unit to load; loads past the wave's last unit re-read it, so the
-    // ring stays unconditional.  With K ranges (KR) a unit's packed index is
-    // t*KTG + c0 + c for (row tile t, range-local k-tile c), walked
-    // incrementally; with one range it is the unit itself.
     int ld_u = u0, ld_t = KR && n > 0 ? u0 / KT : 0, ld_c = KR && n > 0 ? u0 - ld_t * KT : 0;
     auto load = [&](int s) {
-        const uint32_t j = KR ? (uint32_t)(ld_t * KTG + c0 + ld_c) : (uint32_t)ld_u;
+        const uint32_t j = (uint32_t)(ld_t * KTG + c0 + ld_c);
         const bool live = ld_q < n;
         ++ld_q;
         const u32x4_t c = __builtin_amdgcn_raw_buffer_load_b128(
@@ -615,21 +622,20 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             __builtin_amdgcn_make_buffer_rsrc(const_cast<uint2 *>(pscales), 0, (int)(live ? sbytes : 0u), 0x00020000),
             r * 8, j * 128u, 0);
         sw[s] = make_uint2(v.x, v.y);
-        if (KR) {
-            if (ld_u < ulast) {
-                ++ld_u;
-                if (++ld_c == KT) {
-                    ld_c = 0;
-                    ++ld_t;
-                }
+        if (ld_u < ulast) {
+            ++ld_u;
+            if (++ld_c == KT) {
+                ld_c = 0;
+                ++ld_t;
             }
-        } else {
-            ld_u = ld_u < ulast ? ld_u + 1 : ulast;
         }
     };
 #pragma unroll
     for (int s = 0; s < PF; ++s) {
-        load(s);
+        if (KR)
+            load(s);
+        else
+            load_pos(s, s);
         __builtin_amdgcn_sched_barrier(0);
     }
 
@@ -752,8 +758,8 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     };
 
     floatx4_t acc = {0.f, 0.f, 0.f, 0.f};
-    auto tile = [&](int s, int cc) {
-        const uint4 *src = reinterpret_cast<const uint4 *>(xls + cc * xstep);
+    auto tile_x = [&](int s, const uint8_t *xp) {
+        const uint4 *src = reinterpret_cast<const uint4 *>(xp);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             uint2 xf[4];
@@ -773,28 +779,62 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    for (int i = 0; i < n; i += PF) {
+    if (KR) {
+        for (int i = 0; i < n; i += PF) {
 #pragma unroll
-        for (int s = 0; s < PF; ++s) {
-            if (i + s < n) {
-                tile(s, c);
-                ++c;
-                if (c == KT || i + s == n - 1) {
-                    const int cstart = (t == tfirst) ? cfirst : 0;
-                    if (cstart == 0 && c == KT)
-                        store_y(t, acc);                           // whole row tile
-                    else
-                        part[(wave * 2 + (t == tfirst ? 0 : 1)) * 64 + lane] = acc;
-                    acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
-                    if (c == KT) {
-                        c = 0;
-                        ++t;
+            for (int s = 0; s < PF; ++s) {
+                if (i + s < n) {
+                    tile_x(s, xls + c * xstep);
+                    ++c;
+                    if (c == KT || i + s == n - 1) {
+                        const int cstart = (t == tfirst) ? cfirst : 0;
+                        if (cstart == 0 && c == KT)
+                            store_y(t, acc);                           // whole row tile
+                        else
+                            part[(wave * 2 + (t == tfirst ? 0 : 1)) * 64 + lane] = acc;
+                        acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                        if (c == KT) {
+                            c = 0;
+                            ++t;
+                        }
                     }
                 }
+                load(s);
+                __builtin_amdgcn_sched_barrier(0);
             }
-            load(s);
-            __builtin_amdgcn_sched_barrier(0);
         }
+    } else {
+        // countdown to the next row-tile boundary (or the wave's end)
+        int to_flush = KT - cfirst < n ? KT - cfirst : n;
+        const uint8_t *xp = xls + cfirst * xstep;
+        auto unit = [&](int s, int pos) {
+            tile_x(s, xp);
+            xp += xstep;
+            if (--to_flush == 0) {
+                // row tile t done here: whole in this wave, or a part
+                if ((t != tfirst || cfirst == 0) && (t + 1) * KT <= u1)
+                    store_y(t, acc);
+                else
+                    part[(wave * 2 + (t == tfirst ? 0 : 1)) * 64 + lane] = acc;
+                acc = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                ++t;
+                to_flush = n - pos - 1 < KT ? n - pos - 1 : KT;
+                xp = xls;
+            }
+        };
+        int i = 0;
+        for (; i + PF <= n; i += PF) {
+#pragma unroll
+            for (int s = 0; s < PF; ++s) {
+                unit(s, i + s);
+                load_pos(s, i + s + PF);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < PF; ++s)
+            if (i + s < n)
+                unit(s, i + s);
     }
 
     // 5. finish the row tiles split between waves or workgroups
