@@ -84,8 +84,12 @@ size_t q4proj_packed_scales_bytes(int64_t N, int64_t K);
  *   - zero-filled by the caller before its first use; every call that
  *     completes leaves it zero-filled again, so it is reused as is;
  *   - calls that may run at the same time (different streams) need separate
- *     workspaces; a call that faults or is aborted can leave it dirty, after
- *     which it must be zero-filled again.
+ *     workspaces: two kernels swapping words in one workspace corrupt each
+ *     other's sums (silently) and can leave words set;
+ *   - a call that returns an error status enqueued nothing and left the
+ *     workspace as it was; only a kernel that did not run to completion (a
+ *     device fault, a killed process) can leave words set, after which the
+ *     workspace must be zero-filled again before it is reused.
  */
 size_t q4proj_workspace_bytes(int64_t M, int64_t N, int64_t K);
 
@@ -188,6 +192,32 @@ q4proj_status q4proj_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                    float global_scale, const uint16_t *x, uint16_t *h,
                                    int64_t M, int64_t F, int64_t K, void *workspace,
                                    size_t workspace_bytes, void *stream);
+
+/*
+ * q4proj_pack_gate_up — the packed fused gate/up weight built from a
+ * checkpoint's separate gate and up NVFP4 weights.  The FlashRT "Qwen3.6
+ * NVFP4 usage" page (environment-variable table) fuses the MLP gate and up
+ * projections into one NVFP4 projection when the two weights' global scales
+ * are equal; this call is that fusion at load time.
+ * In:  gate_codes, up_codes  uint8 [F][K/2] canonical codes, 8-byte aligned
+ *      gate_scales, up_scales uint8 [F][K/16] canonical e4m3 scales
+ *      gate_global_scale, up_global_scale: the two weights' global scales,
+ *      which must be equal bit for bit (the fused projections take one g);
+ *      F % 8 == 0.
+ * Out: packed_codes (q4proj_packed_codes_bytes(2F, K) bytes, 16-byte aligned)
+ *      and packed_scales (q4proj_packed_scales_bytes(2F, K) bytes): the same
+ *      bytes q4proj_pack writes for the [2F][K] weight whose rows alternate
+ *      8 gate rows and the matching 8 up rows (the layout q4proj_gemv_silu_mul
+ *      and q4proj_gemm_silu_mul read).  A pure byte permutation.
+ * Errors: EINVAL (null pointer, F <= 0, F % 8 != 0, K <= 0, K % 16 != 0,
+ *         unequal or NaN global scales, misaligned buffers, an output
+ *         overlapping an input or the other output), EDEVICE, EHIP.
+ */
+q4proj_status q4proj_pack_gate_up(const uint8_t *gate_codes, const uint8_t *gate_scales,
+                                  const uint8_t *up_codes, const uint8_t *up_scales,
+                                  float gate_global_scale, float up_global_scale, int64_t F,
+                                  int64_t K, uint8_t *packed_codes, uint8_t *packed_scales,
+                                  void *stream);
 
 /*
  * q4proj_gemm_silu_mul — the same fused gate/up projection and epilogue as

@@ -41,6 +41,8 @@ _lib.q4proj_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.q4proj_workspace_bytes.restype = _sz
 _lib.q4proj_pack.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
 _lib.q4proj_pack.restype = ctypes.c_int
+_lib.q4proj_pack_gate_up.argtypes = [_vp, _vp, _vp, _vp, _f32, _f32, _i64, _i64, _vp, _vp, _vp]
+_lib.q4proj_pack_gate_up.restype = ctypes.c_int
 _lib.q4proj_unpack.argtypes = [_vp, _vp, _i64, _i64, _vp, _vp, _vp]
 _lib.q4proj_unpack.restype = ctypes.c_int
 _PROJ_ARGS = [_vp, _vp, _f32, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp]
@@ -70,7 +72,7 @@ _lib.q4proj_last_hip_error.restype = ctypes.c_char_p
 
 #: Exported symbols declared by include/q4proj.h.
 SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
-           "q4proj_pack", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
+           "q4proj_pack", "q4proj_pack_gate_up", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
            "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul", "q4proj_gemm_silu_mul",
            "q4proj_argmax_workspace_bytes", "q4proj_gemv_argmax",
            "q4proj_quantize_workspace_bytes", "q4proj_quantize",
@@ -145,12 +147,13 @@ def _guard(dev: int):
 
 
 def _stream(dev: int, stream):
-    """hipStream_t of `stream`, or of device dev's current stream."""
+    """hipStream_t of `stream` (a torch stream or a raw handle), or of device
+    dev's current stream."""
     if stream is None:
         if _raw_stream is not None:
             return _raw_stream(dev)
         stream = torch.cuda.current_stream(dev)
-    return stream.cuda_stream
+    return stream if isinstance(stream, int) else stream.cuda_stream
 
 
 def _need(t: torch.Tensor, name: str, dtype, numel: int, dev: int):
@@ -180,6 +183,27 @@ def q4proj_pack(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int,
                                 packed_scales.data_ptr(), _stream(dev, stream)), "q4proj_pack")
 
 
+def q4proj_pack_gate_up(gate_codes, gate_scales, up_codes, up_scales, gate_global_scale: float,
+                        up_global_scale: float, F: int, K: int, packed_codes, packed_scales,
+                        stream=None) -> None:
+    """Separate canonical gate and up weights (u8 [F][K/2] codes, [F][K/16]
+    scales, equal global scales) -> the packed fused [2F][K] gate/up weight
+    (8 gate rows and 8 up rows alternating)."""
+    dev = _dev(gate_codes, "gate_codes")
+    for t, name in ((gate_codes, "gate_codes"), (up_codes, "up_codes")):
+        _need(t, name, torch.uint8, F * (K // 2), dev)
+    for t, name in ((gate_scales, "gate_scales"), (up_scales, "up_scales")):
+        _need(t, name, torch.uint8, F * (K // 16), dev)
+    _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(2 * F, K), dev)
+    _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(2 * F, K), dev)
+    with _guard(dev):
+        _check(_lib.q4proj_pack_gate_up(gate_codes.data_ptr(), gate_scales.data_ptr(),
+                                        up_codes.data_ptr(), up_scales.data_ptr(),
+                                        float(gate_global_scale), float(up_global_scale), F, K,
+                                        packed_codes.data_ptr(), packed_scales.data_ptr(),
+                                        _stream(dev, stream)), "q4proj_pack_gate_up")
+
+
 def q4proj_unpack(packed_codes: torch.Tensor, packed_scales: torch.Tensor, N: int, K: int,
                   codes: torch.Tensor, scales: torch.Tensor, stream=None) -> None:
     dev = _dev(packed_codes, "packed_codes")
@@ -196,18 +220,42 @@ def q4proj_unpack(packed_codes: torch.Tensor, packed_scales: torch.Tensor, N: in
 _workspaces: dict = {}
 
 
-def default_workspace(device, nbytes: int):
-    """A zero-filled device buffer of at least nbytes, one per device, reused by
-    every call that passes no workspace (calls leave it zero-filled).  Calls
-    that may run concurrently on one device need workspaces of their own."""
+def _stream_handle_and_obj(dev: int, stream):
+    """(raw hipStream_t, torch stream object) of `stream`, or of device dev's
+    current stream when stream is None."""
+    if stream is None:
+        obj = torch.cuda.current_stream(dev)
+        return obj.cuda_stream, obj
+    if isinstance(stream, torch.cuda.Stream):
+        return stream.cuda_stream, stream
+    handle = int(stream)
+    return handle, torch.cuda.ExternalStream(handle, device=torch.device("cuda", dev))
+
+
+def default_workspace(device, nbytes: int, stream=None):
+    """A zero-filled device buffer of at least nbytes for calls on `stream`
+    (default: the device's current stream) that pass no workspace.
+
+    One buffer per (device, stream): calls on one stream run in order, so
+    they can share it (each call leaves it zero-filled); calls on different
+    streams get different buffers and may run concurrently.  The buffer is
+    allocated and zero-filled on that stream, so the fill is ordered before
+    the calls that use it, and torch's caching allocator ties the memory to
+    that stream.  A call that returned an error enqueued nothing and left
+    the buffer as it was; only a kernel that did not run to completion (a
+    device fault, a killed process) can leave words set, and the process's
+    device state is then lost anyway."""
     if nbytes <= 0:
         return None
-    key = device if isinstance(device, int) else (
+    dev = device if isinstance(device, int) else (
         torch.device(device).index if torch.device(device).index is not None
         else torch.cuda.current_device())
+    key = (dev, _stream(dev, stream))
     ws = _workspaces.get(key)
     if ws is None or ws.numel() < nbytes:
-        ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", key))
+        _, sobj = _stream_handle_and_obj(dev, stream)
+        with torch.cuda.stream(sobj):
+            ws = torch.zeros(nbytes, dtype=torch.uint8, device=torch.device("cuda", dev))
         _workspaces[key] = ws
     return ws
 
@@ -230,7 +278,7 @@ def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, w
     _need(y, "y", torch.float32, M * N, dev)
     ws_ptr, ws_bytes = None, 0
     if workspace is None and fn is _lib.q4proj_gemv:
-        workspace = default_workspace(dev, q4proj_workspace_bytes(M, N, K))
+        workspace = default_workspace(dev, q4proj_workspace_bytes(M, N, K), stream)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
@@ -281,7 +329,7 @@ def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, 
     _need(h, "h", h.dtype, M * F, dev)
     ws_ptr, ws_bytes = None, 0
     if workspace is None and fn is _lib.q4proj_gemv_silu_mul:
-        workspace = default_workspace(dev, q4proj_silu_mul_workspace_bytes(M, F, K))
+        workspace = default_workspace(dev, q4proj_silu_mul_workspace_bytes(M, F, K), stream)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
@@ -310,7 +358,7 @@ def q4proj_gemv_argmax(packed_codes, packed_scales, global_scale: float, x, y, m
     _need(max_val, "max_val", torch.float32, M, dev)
     _need(max_idx, "max_idx", torch.int64, M, dev)
     if workspace is None:
-        workspace = default_workspace(dev, q4proj_argmax_workspace_bytes(M, N, K))
+        workspace = default_workspace(dev, q4proj_argmax_workspace_bytes(M, N, K), stream)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
@@ -338,8 +386,12 @@ def q4proj_quantize(w, N: int, K: int, codes: torch.Tensor, scales: torch.Tensor
     _need(scales, "scales", torch.uint8, N * (K // 16), dev)
     _need(global_scale, "global_scale", torch.float32, 1, dev)
     if workspace is None:
-        workspace = torch.empty(q4proj_quantize_workspace_bytes(N, K), dtype=torch.uint8,
-                                device=dev)
+        # a temporary allocated on the stream the kernels run on, so that the
+        # caching allocator does not hand it out again before they are done
+        _, sobj = _stream_handle_and_obj(dev, stream)
+        with torch.cuda.stream(sobj):
+            workspace = torch.empty(q4proj_quantize_workspace_bytes(N, K), dtype=torch.uint8,
+                                    device=torch.device("cuda", dev))
     _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
     with _guard(dev):
         _check(_lib.q4proj_quantize(w.data_ptr(), N, K, codes.data_ptr(), scales.data_ptr(),
@@ -349,18 +401,38 @@ def q4proj_quantize(w, N: int, K: int, codes: torch.Tensor, scales: torch.Tensor
 
 def quantize_weight(w, N: int, K: int, stream=None):
     """Allocate canonical codes/scales and a device global scale on w.device
-    and fill them with q4proj_quantize."""
+    (on the stream the quantizer runs on) and fill them with q4proj_quantize."""
     dev = w.device
-    codes = torch.empty(N * (K // 2), dtype=torch.uint8, device=dev)
-    scales = torch.empty(N * (K // 16), dtype=torch.uint8, device=dev)
-    g = torch.empty(1, dtype=torch.float32, device=dev)
+    _, sobj = _stream_handle_and_obj(_dev(w, "w"), stream)
+    with torch.cuda.stream(sobj):
+        codes = torch.empty(N * (K // 2), dtype=torch.uint8, device=dev)
+        scales = torch.empty(N * (K // 16), dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
     q4proj_quantize(w, N, K, codes, scales, g, stream=stream)
     return codes, scales, g
 
 
+def pack_gate_up_weight(gate_codes, gate_scales, up_codes, up_scales, gate_global_scale: float,
+                        up_global_scale: float, F: int, K: int, stream=None):
+    """Allocate the packed fused gate/up buffers on gate_codes.device and fill
+    them with q4proj_pack_gate_up."""
+    _, sobj = _stream_handle_and_obj(_dev(gate_codes, "gate_codes"), stream)
+    with torch.cuda.stream(sobj):
+        pc = torch.empty(q4proj_packed_codes_bytes(2 * F, K), dtype=torch.uint8,
+                         device=gate_codes.device)
+        ps = torch.empty(q4proj_packed_scales_bytes(2 * F, K), dtype=torch.uint8,
+                         device=gate_codes.device)
+    q4proj_pack_gate_up(gate_codes, gate_scales, up_codes, up_scales, gate_global_scale,
+                        up_global_scale, F, K, pc, ps, stream)
+    return pc, ps
+
+
 def pack_weight(codes: torch.Tensor, scales: torch.Tensor, N: int, K: int, stream=None):
-    """Allocate packed buffers on codes.device and fill them with q4proj_pack."""
-    pc = torch.empty(q4proj_packed_codes_bytes(N, K), dtype=torch.uint8, device=codes.device)
-    ps = torch.empty(q4proj_packed_scales_bytes(N, K), dtype=torch.uint8, device=codes.device)
+    """Allocate packed buffers on codes.device (on the stream the swizzle runs
+    on) and fill them with q4proj_pack."""
+    _, sobj = _stream_handle_and_obj(_dev(codes, "codes"), stream)
+    with torch.cuda.stream(sobj):
+        pc = torch.empty(q4proj_packed_codes_bytes(N, K), dtype=torch.uint8, device=codes.device)
+        ps = torch.empty(q4proj_packed_scales_bytes(N, K), dtype=torch.uint8, device=codes.device)
     q4proj_pack(codes, scales, N, K, pc, ps, stream)
     return pc, ps

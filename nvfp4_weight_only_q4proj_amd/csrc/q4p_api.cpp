@@ -153,6 +153,42 @@ q4proj_status q4proj_pack(const uint8_t *codes, const uint8_t *scales, int64_t N
                                        static_cast<hipStream_t>(stream)));
 }
 
+q4proj_status q4proj_pack_gate_up(const uint8_t *gate_codes, const uint8_t *gate_scales,
+                                  const uint8_t *up_codes, const uint8_t *up_scales,
+                                  float gate_global_scale, float up_global_scale, int64_t F,
+                                  int64_t K, uint8_t *packed_codes, uint8_t *packed_scales,
+                                  void *stream)
+{
+    if (!gate_codes || !gate_scales || !up_codes || !up_scales || !packed_codes || !packed_scales)
+        return Q4P_EINVAL;
+    if (F < 8 || F % 8 != 0 || !shape_ok(2 * F, K))
+        return Q4P_EINVAL;
+    // one global scale multiplies the fused projection: both halves need the
+    // same one (bit for bit; a NaN never equals itself)
+    if (!(gate_global_scale == up_global_scale) ||
+        std::memcmp(&gate_global_scale, &up_global_scale, sizeof(float)) != 0)
+        return Q4P_EINVAL;
+    if (!aligned(gate_codes, 8) || !aligned(up_codes, 8) || !aligned(packed_codes, 16) ||
+        !aligned(packed_scales, 8))
+        return Q4P_EINVAL;
+    const size_t pcb = q4proj_packed_codes_bytes(2 * F, K);
+    const size_t psb = q4proj_packed_scales_bytes(2 * F, K);
+    const size_t cb = (size_t)F * (size_t)(K / 2), sb = (size_t)F * (size_t)(K / 16);
+    const void *in[4] = {gate_codes, gate_scales, up_codes, up_scales};
+    const size_t inb[4] = {cb, sb, cb, sb};
+    for (int i = 0; i < 4; ++i)
+        if (overlap(packed_codes, pcb, in[i], inb[i]) || overlap(packed_scales, psb, in[i], inb[i]))
+            return Q4P_EINVAL;
+    if (overlap(packed_codes, pcb, packed_scales, psb))
+        return Q4P_EINVAL;
+    q4proj_status st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_pack_gate_up(gate_codes, gate_scales, up_codes, up_scales, F, K,
+                                               packed_codes, packed_scales,
+                                               static_cast<hipStream_t>(stream)));
+}
+
 q4proj_status q4proj_unpack(const uint8_t *packed_codes, const uint8_t *packed_scales, int64_t N,
                             int64_t K, uint8_t *codes, uint8_t *scales, void *stream)
 {

@@ -11,6 +11,13 @@ namespace q4p {
 hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, int64_t N, int64_t K,
                        uint8_t *packed_codes, uint8_t *packed_scales, hipStream_t stream);
 
+// The fused gate/up weight's packed layout from two canonical [F][K]
+// weights (F % 8 == 0): rows alternate 8 gate rows and 8 up rows.
+hipError_t launch_pack_gate_up(const uint8_t *gate_codes, const uint8_t *gate_scales,
+                               const uint8_t *up_codes, const uint8_t *up_scales, int64_t F,
+                               int64_t K, uint8_t *packed_codes, uint8_t *packed_scales,
+                               hipStream_t stream);
+
 hipError_t launch_unpack(const uint8_t *packed_codes, const uint8_t *packed_scales, int64_t N,
                          int64_t K, uint8_t *codes, uint8_t *scales, hipStream_t stream);
 

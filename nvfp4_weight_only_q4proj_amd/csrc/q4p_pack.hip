@@ -4,6 +4,12 @@
 // scales [N][K/16]) and the tiled layout described in q4p_device.h.  One
 // thread moves one (tile, row) pair: 64 canonical code bytes (one row of a
 // 16 x 128 tile) become four 16-byte lane slots, and 8 scale bytes move as is.
+//
+// The fused gate/up pack reads two canonical [F][K] weights (a checkpoint's
+// separate gate and up projections) and writes the packed layout of the
+// [2F][K] weight whose rows alternate 8 gate rows and the matching 8 up rows:
+// row 16t + r of the fused weight is gate row 8t + r for r < 8 and up row
+// 8t + r - 8 otherwise.
 #include "q4p_device.h"
 #include "q4p_launch.h"
 
@@ -39,8 +45,12 @@ __device__ __forceinline__ void load_row_codes(const uint8_t *codes, int64_t N, 
     }
 }
 
+// FUSE: rows of the fused gate/up weight from (codes, scales) = gate and
+// (codes2, scales2) = up, each with N rows; otherwise one weight of N rows.
+template <bool FUSE>
 __global__ void __launch_bounds__(256)
-pack_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales, int64_t N,
+pack_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scales,
+            const uint8_t *__restrict__ codes2, const uint8_t *__restrict__ scales2, int64_t N,
             int64_t K, int64_t KT, int64_t total, uint8_t *__restrict__ pcodes,
             uint8_t *__restrict__ pscales)
 {
@@ -50,10 +60,19 @@ pack_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scale
     const int r = (int)(idx & 15);
     const int64_t tc = idx >> 4;               // tile index t*KT + c
     const int64_t t = tc / KT, c = tc % KT;
-    const int64_t n = 16 * t + r;
+    // source weight and row of packed row 16t + r
+    const uint8_t *src_codes = codes, *src_scales = scales;
+    int64_t n = 16 * t + r;
+    if (FUSE) {
+        if (r >= 8) {
+            src_codes = codes2;
+            src_scales = scales2;
+        }
+        n = 8 * t + (r & 7);
+    }
 
     uint16_t u[32];                            // u[4b + g]: block b, k-group g
-    load_row_codes(codes, N, K, n, c, u);
+    load_row_codes(src_codes, N, K, n, c, u);
     uint4 *dst = reinterpret_cast<uint4 *>(pcodes + tc * kTileCodeBytes);
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
@@ -70,7 +89,7 @@ pack_kernel(const uint8_t *__restrict__ codes, const uint8_t *__restrict__ scale
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
         const int64_t kb = 8 * c + b;
-        uint32_t v = (n < N && kb < row_blocks) ? scales[n * row_blocks + kb] : 0u;
+        uint32_t v = (n < N && kb < row_blocks) ? src_scales[n * row_blocks + kb] : 0u;
         s[b >> 2] |= v << (8 * (b & 3));
     }
     uint2 so;
@@ -148,8 +167,22 @@ hipError_t launch_pack(const uint8_t *codes, const uint8_t *scales, int64_t N, i
     const int64_t KT = k_tiles(K);
     const int64_t total = n_tiles(N) * KT * 16;
     const int64_t blocks = (total + 255) / 256;
-    hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, codes, scales,
-                       N, K, KT, total, packed_codes, packed_scales);
+    hipLaunchKernelGGL(pack_kernel<false>, dim3((unsigned)blocks), dim3(256), 0, stream, codes,
+                       scales, codes, scales, N, K, KT, total, packed_codes, packed_scales);
+    return hipGetLastError();
+}
+
+hipError_t launch_pack_gate_up(const uint8_t *gate_codes, const uint8_t *gate_scales,
+                               const uint8_t *up_codes, const uint8_t *up_scales, int64_t F,
+                               int64_t K, uint8_t *packed_codes, uint8_t *packed_scales,
+                               hipStream_t stream)
+{
+    const int64_t KT = k_tiles(K);
+    const int64_t total = n_tiles(2 * F) * KT * 16;
+    const int64_t blocks = (total + 255) / 256;
+    hipLaunchKernelGGL(pack_kernel<true>, dim3((unsigned)blocks), dim3(256), 0, stream, gate_codes,
+                       gate_scales, up_codes, up_scales, F, K, KT, total, packed_codes,
+                       packed_scales);
     return hipGetLastError();
 }
 

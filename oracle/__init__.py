@@ -221,6 +221,21 @@ def silu_mul_cols(codes, scales, g: float, x, F: int, cols=None, nthreads=None, 
     return h, bound
 
 
+def silu_mul_separate(gate_codes, gate_scales, up_codes, up_scales, g: float, x, nthreads=None,
+                      lib=None):
+    """h[M][F] = silu(gate) * up in fp64 from two separate [F][K] weights with
+    the one global scale g (the plain definition of the fused projection,
+    no row interleave), and the allowance bound of the fp32 path before its
+    bf16 rounding."""
+    lib = lib or load()
+    a, Sa = proj(gate_codes, gate_scales, g, x, nthreads, lib)
+    b, Sb = proj(up_codes, up_scales, g, x, nthreads, lib)
+    h = silu_mul(a, b, lib)
+    bound = np.empty_like(h)
+    lib.orc_silu_mul_bound(h.size, _ptr(a), _ptr(b), _ptr(Sa), _ptr(Sb), float(RTOL), _ptr(bound))
+    return h, bound
+
+
 def check_bf16(h_ref, bound, h_gpu_bits, lib=None):
     """Returns (number of failing elements, max |h-h_ref| / allowance)."""
     hr = np.ascontiguousarray(h_ref, dtype=np.float64)

@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(q4):
     names = declared_functions()
-    assert len(names) == 16, names
+    assert len(names) == 17, names
     lib = q4.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -225,6 +225,24 @@ def test_pack_validation(q4, fn):
     assert f(A, B, 16, 128, X + 4, Y, None) == q4.EINVAL
 
 
+def test_pack_gate_up_validation(q4):
+    """Fused gate/up pack: F a positive multiple of 8, equal (non-NaN) global
+    scales, aligned and non-overlapping buffers; host checks only."""
+    lib = q4.library()
+    one = ctypes.c_float(1.0)
+
+    def f(gc=A, gs=B, uc=A + 65536, us=B + 65536, g1=one, g2=one, F=16, K=128, pc=X, ps=Y):
+        return lib.q4proj_pack_gate_up(gc, gs, uc, us, g1, g2, F, K, pc, ps, None)
+
+    for kw in [dict(gc=None), dict(us=None), dict(pc=None), dict(F=0), dict(F=12), dict(F=4),
+               dict(K=120), dict(K=0), dict(g2=ctypes.c_float(2.0)),
+               dict(g1=ctypes.c_float(float("nan")), g2=ctypes.c_float(float("nan"))),
+               dict(g1=ctypes.c_float(0.0), g2=ctypes.c_float(-0.0)),
+               dict(gc=A + 4), dict(pc=X + 8), dict(ps=Y + 4), dict(pc=A), dict(ps=B + 65536),
+               dict(ps=X)]:
+        assert f(**kw) == q4.EINVAL, kw
+
+
 def test_status_strings(q4):
     lib = q4.library()
     for s in range(6):
@@ -241,6 +259,8 @@ def test_no_device_no_fallback(q4):
     assert proj(lib, "q4proj_gemm", M=512) == q4.EDEVICE
     assert proj(lib, "q4proj_gemm", M=512, ws=None, wsb=0) == q4.EDEVICE   # gemm needs none
     assert lib.q4proj_pack(A, B, 16, 128, X, Y, None) == q4.EDEVICE
+    assert lib.q4proj_pack_gate_up(A, B, A + 65536, B + 65536, ctypes.c_float(0.5),
+                                   ctypes.c_float(0.5), 16, 128, X, Y, None) == q4.EDEVICE
     assert silu(lib) == q4.EDEVICE
     assert silu(lib, h=Y + 2) == q4.EDEVICE             # bf16 out needs 2-byte alignment only
     assert silu(lib, fn="q4proj_gemm_silu_mul", M=512, ws=None, wsb=0) == q4.EDEVICE
