@@ -150,6 +150,29 @@ q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_sca
                           void *stream);
 
 /*
+ * q4proj_gemv_noalloc — q4proj_gemv for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation): the same projection, arguments and result as
+ * q4proj_gemv, without the workspace.  The exchange words live in a device
+ * array inside the library instead: 8 MiB per GPU, allocated when the
+ * library's code is loaded on that GPU and held until the process ends;
+ * the call itself allocates and frees nothing.
+ * Limit: shapes whose q4proj_workspace_bytes(M, N, K) exceeds 8 MiB return
+ * EWORKSPACE before any launch (e.g. M >= 13 on a 248320 x 5120 lm-head);
+ * every M = 1 shape the stream-K GEMV serves fits.
+ * State: all calls on one GPU share that GPU's array.  It is zero-filled on
+ * the first call on each GPU (by a kernel on that call's stream) and every
+ * completed call leaves it zero-filled, so calls issued one after another
+ * need nothing more.  Calls that may overlap on one GPU (different streams
+ * without ordering between them) race on the array and corrupt each other's
+ * results: serialise them, or use q4proj_gemv with separate workspaces.
+ * Errors: as q4proj_gemv, with EWORKSPACE for shapes beyond the limit.
+ */
+q4proj_status q4proj_gemv_noalloc(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                  float global_scale, const uint16_t *x, float *y, int64_t M,
+                                  int64_t N, int64_t K, void *stream);
+
+/*
  * Device scratch q4proj_gemv_silu_mul needs for (M, F, K):
  *     8 * (65536 + (KS - 1) * M * F) bytes,
  * with KS the number of K ranges as for q4proj_gemv (the joins carry a gate

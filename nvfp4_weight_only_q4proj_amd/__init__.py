@@ -50,6 +50,8 @@ _lib.q4proj_gemv.argtypes = _PROJ_ARGS
 _lib.q4proj_gemv.restype = ctypes.c_int
 _lib.q4proj_gemm.argtypes = _PROJ_ARGS
 _lib.q4proj_gemm.restype = ctypes.c_int
+_lib.q4proj_gemv_noalloc.argtypes = [_vp, _vp, _f32, _vp, _vp, _i64, _i64, _i64, _vp]
+_lib.q4proj_gemv_noalloc.restype = ctypes.c_int
 _lib.q4proj_silu_mul_workspace_bytes.argtypes = [_i64, _i64, _i64]
 _lib.q4proj_silu_mul_workspace_bytes.restype = _sz
 _lib.q4proj_gemv_silu_mul.argtypes = _PROJ_ARGS
@@ -73,6 +75,7 @@ _lib.q4proj_last_hip_error.restype = ctypes.c_char_p
 #: Exported symbols declared by include/q4proj.h.
 SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
            "q4proj_pack", "q4proj_pack_gate_up", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
+           "q4proj_gemv_noalloc",
            "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul", "q4proj_gemm_silu_mul",
            "q4proj_argmax_workspace_bytes", "q4proj_gemv_argmax",
            "q4proj_quantize_workspace_bytes", "q4proj_quantize",
@@ -293,6 +296,22 @@ def q4proj_gemv(packed_codes, packed_scales, global_scale: float, x, y, M: int, 
     """y[M][N] fp32 = x[M][K] bf16 . dequant(W)^T for 1 <= M <= 16."""
     _proj(_lib.q4proj_gemv, "q4proj_gemv", packed_codes, packed_scales, global_scale, x, y, M, N,
           K, workspace, stream)
+
+
+def q4proj_gemv_noalloc(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int,
+                        K: int, stream=None) -> None:
+    """q4proj_gemv with the library's per-GPU scratch array in place of a
+    workspace (allocates nothing; calls that overlap on one GPU race)."""
+    dev = _dev(x, "x")
+    _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
+    _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
+    x = _bf16_bits(x, "x")
+    _need(x, "x", x.dtype, M * K, dev)
+    _need(y, "y", torch.float32, M * N, dev)
+    with _guard(dev):
+        _check(_lib.q4proj_gemv_noalloc(packed_codes.data_ptr(), packed_scales.data_ptr(),
+                                        float(global_scale), x.data_ptr(), y.data_ptr(), M, N, K,
+                                        _stream(dev, stream)), "q4proj_gemv_noalloc")
 
 
 def q4proj_gemm(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,

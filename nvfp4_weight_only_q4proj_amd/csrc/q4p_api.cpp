@@ -234,6 +234,26 @@ q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_sca
                                        workspace, static_cast<hipStream_t>(stream)));
 }
 
+q4proj_status q4proj_gemv_noalloc(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                                  float global_scale, const uint16_t *x, float *y, int64_t M,
+                                  int64_t N, int64_t K, void *stream)
+{
+    // the library's scratch array stands in for the workspace: a shape whose
+    // exchange words do not fit is refused (EWORKSPACE) before any launch
+    const size_t need = q4proj_workspace_bytes(M, N, K);
+    q4proj_status st = check_projection(packed_codes, packed_scales, x, y, M, N, K,
+                                        q4p::gemv_noalloc_max_bytes(), need);
+    if (st != Q4P_OK)
+        return st;
+    if (M > Q4PROJ_GEMV_MAX_M)
+        return Q4P_EUNSUPPORTED;
+    st = check_device();
+    if (st != Q4P_OK)
+        return st;
+    return record_hip(q4p::launch_gemv_noalloc(packed_codes, packed_scales, global_scale, x, y, M,
+                                               N, K, static_cast<hipStream_t>(stream)));
+}
+
 size_t q4proj_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K)
 {
     if (M <= 0 || M > Q4PROJ_GEMV_MAX_M || F <= 0 || F % 8 != 0 || F > ((int64_t)1 << 29) ||

@@ -48,6 +48,13 @@
 #include "q4p_device.h"
 #include "q4p_launch.h"
 
+// Exchange words of q4proj_gemv_noalloc: a device array inside the library
+// (one copy per GPU, held until the process ends) in place of the caller's
+// workspace.  Host code never uses this name as an address: it asks the
+// runtime for each device's address once and passes that to the kernels.
+static constexpr size_t kScratchBytes = 8u << 20;
+static __device__ __align__(256) unsigned long long scratch[kScratchBytes / 8];
+
 namespace q4p {
 
 namespace {
@@ -1263,6 +1270,62 @@ hipError_t launch_gemv_argmax(const uint8_t *packed_codes, const uint8_t *packed
                        reinterpret_cast<const uint2 *>(packed_scales), x, y,
                        static_cast<unsigned long long *>(workspace), args);
     return hipGetLastError();
+}
+
+namespace {
+
+__global__ void __launch_bounds__(256) scratch_clear_kernel(unsigned long long *p, size_t words)
+{
+    for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < words; i += (size_t)gridDim.x * 256)
+        p[i] = 0ull;
+}
+
+// Per-device address of the scratch array (the runtime's address for the
+// device that is current), looked up once per device; the array is cleared
+// on the first call on each device, on that call's stream.
+struct ScratchSlot {
+    unsigned long long *ptr;
+    bool cleared;
+};
+
+}  // namespace
+
+size_t gemv_noalloc_max_bytes() { return kScratchBytes; }
+
+hipError_t launch_gemv_noalloc(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                               float g, const uint16_t *x, float *y, int64_t M, int64_t N,
+                               int64_t K, hipStream_t stream)
+{
+    static std::mutex mu;
+    static ScratchSlot slots[64];
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess)
+        return e;
+    if (dev < 0 || dev >= 64)
+        return hipErrorInvalidDevice;
+    unsigned long long *ptr = nullptr;
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        ScratchSlot &sl = slots[dev];
+        if (sl.ptr == nullptr) {
+            void *p = nullptr;
+            e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+            if (e != hipSuccess)
+                return e;
+            sl.ptr = static_cast<unsigned long long *>(p);
+        }
+        if (!sl.cleared) {
+            hipLaunchKernelGGL(scratch_clear_kernel, dim3(256), dim3(256), 0, stream, sl.ptr,
+                               kScratchBytes / 8);
+            e = hipGetLastError();
+            if (e != hipSuccess)
+                return e;
+            sl.cleared = true;
+        }
+        ptr = sl.ptr;
+    }
+    return launch_gemv(packed_codes, packed_scales, g, x, y, M, N, K, ptr, stream);
 }
 
 }  // namespace q4p

@@ -29,6 +29,14 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
                        void *workspace, hipStream_t stream);
 
+// launch_gemv with the library's per-device scratch array as the workspace
+// (no allocation); shapes whose workspace exceeds gemv_noalloc_max_bytes()
+// must be refused by the caller.
+size_t gemv_noalloc_max_bytes();
+hipError_t launch_gemv_noalloc(const uint8_t *packed_codes, const uint8_t *packed_scales,
+                               float g, const uint16_t *x, float *y, int64_t M, int64_t N,
+                               int64_t K, hipStream_t stream);
+
 // Fused gate/up projection + silu(gate)*up (weight of 2F rows, gate and up
 // rows alternating in blocks of 8), for the shapes the stream-K GEMV serves,
 // F % 8 == 0.

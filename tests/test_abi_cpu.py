@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(q4):
     names = declared_functions()
-    assert len(names) == 17, names
+    assert len(names) == 18, names
     lib = q4.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -243,6 +243,22 @@ def test_pack_gate_up_validation(q4):
         assert f(**kw) == q4.EINVAL, kw
 
 
+def test_gemv_noalloc_validation(q4):
+    """The allocation-free GEMV checks its arguments as q4proj_gemv does and
+    refuses shapes whose exchange words exceed its 8 MiB array."""
+    lib = q4.library()
+    f = lib.q4proj_gemv_noalloc
+    one = ctypes.c_float(1.0)
+    assert f(None, B, one, X, Y, 1, 64, 256, None) == q4.EINVAL
+    assert f(A, B, one, X, None, 1, 64, 256, None) == q4.EINVAL
+    assert f(A, B, one, X, Y, 1, 64, 250, None) == q4.EINVAL
+    assert f(A, B, one, X + 8, Y, 1, 64, 256, None) == q4.EINVAL
+    assert f(A, B, one, X, Y, 17, 64, 256, None) == q4.EUNSUPPORTED
+    # 16 rows on the lm-head shape: 512 KiB + 8 * 16 * 248320 B of words
+    assert q4.q4proj_workspace_bytes(16, 248320, 5120) > 8 << 20
+    assert f(A, B, one, X, W, 16, 248320, 5120, None) == q4.EWORKSPACE
+
+
 def test_status_strings(q4):
     lib = q4.library()
     for s in range(6):
@@ -259,6 +275,7 @@ def test_no_device_no_fallback(q4):
     assert proj(lib, "q4proj_gemm", M=512) == q4.EDEVICE
     assert proj(lib, "q4proj_gemm", M=512, ws=None, wsb=0) == q4.EDEVICE   # gemm needs none
     assert lib.q4proj_pack(A, B, 16, 128, X, Y, None) == q4.EDEVICE
+    assert lib.q4proj_gemv_noalloc(A, B, ctypes.c_float(1.0), X, Y, 1, 64, 256, None) == q4.EDEVICE
     assert lib.q4proj_pack_gate_up(A, B, A + 65536, B + 65536, ctypes.c_float(0.5),
                                    ctypes.c_float(0.5), 16, 128, X, Y, None) == q4.EDEVICE
     assert silu(lib) == q4.EDEVICE
