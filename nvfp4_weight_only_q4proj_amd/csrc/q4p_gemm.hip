@@ -8,8 +8,10 @@
 //    about one workgroup per CU (256), e.g. T = 17 for N = 17408 and T = 14
 //    for N = 14336 at M = 512: 256 equal workgroups, no tail wave.
 //  * Waves w and w+4 (one SIMD) own the same outputs and split every k-tile:
-//    wave w takes its first two 32-wide k-steps, wave w+4 the last two, and
-//    the two partial sums are added through LDS at the end.
+//    wave w takes its first two 32-wide k-steps, wave w+4 the last two.  At
+//    the end each hands the other, through LDS, the half of its partial sums
+//    that the other finishes (four of the eight 16-row blocks of every tile),
+//    so both waves of a SIMD share the epilogue.
 //  * Each wave pair owns Q = T/4 whole weight tiles (all 128 rows) plus a
 //    share of the RT = T%4 remaining tiles: half of one tile (64 rows) when
 //    RT = 2, a quarter (32 rows) of each otherwise, so all waves do the same
@@ -334,7 +336,10 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     // afterwards every k-tile issues the loads of the k-tile two ahead
     issue_stage(0, true, sx0, sw0);
     issue_stage(1, KT > 1, sx1, sw1);
-    __builtin_amdgcn_s_waitcnt(kWaitVm0);
+    // stage 1's loads (the last kLoads issued) may still be in flight; the
+    // first k-tile's barrier waits for them
+    static_assert(kLoads < 16, "vmcnt immediate");
+    __builtin_amdgcn_s_waitcnt(0x0f70 | kLoads);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
 #pragma unroll
@@ -351,7 +356,21 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     }
 
 
-    // ---- add the k-halves: waves 4..7 hand their sums to waves 0..3 --------
+    // ---- add the k-halves ------------------------------------------------------
+    // Wave kh finishes row-block positions 4kh..4kh+3 of its whole tiles and
+    // the kh-th half of its remaining-tile blocks.  Both waves of a pair hand
+    // the partner the half it finishes, all through LDS at once: fragment f
+    // (64 lanes x 16 bytes) of wave v sits in its own slot of the now free
+    // stage buffers, so one barrier separates the writes from the reads, and
+    // both waves of a SIMD then share the epilogue.
+    constexpr int HR = RR / 2;                                 // remaining blocks kept per wave
+    constexpr int kKeep = 4 * Q + RB * HR;                     // fragments kept (and handed over)
+    static_assert(kKeep <= 8 || 2 * (kKeep - 8 < 8 ? kKeep - 8 : 8) * 1024 <= kWStageBytes,
+                  "fragments 8..15 of waves 4..7: two waves per weight stage");
+    static_assert(kKeep <= 16 || (kKeep <= 18 && 8 * 2048 <= kWStageBytes),
+                  "fragments 16, 17: the third weight stage");
+    static_assert(3 * (kXStageBytes + kWStageBytes) <= 160 * 1024, "LDS of one CU");
+    floatx4_t keep[kKeep > 0 ? kKeep : 1];
     {
         // every wave is past its last LDS read of the stages (the last
         // compute ended with them) and its trailing zero-writing loads have
@@ -359,115 +378,96 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
-        constexpr int kAcc = 8 * Q + RB * RR;                // floatx4 per lane
-        // one slot per wave pair: three activation stages and one weight
-        // stage, each holding kPass fragments of 64 lanes x 16 bytes
-        constexpr int kPass = kWStageBytes / (64 * 16);
-        floatx4_t *red = reinterpret_cast<floatx4_t *>(w < 2 ? (w == 0 ? sx0 : sx1) : (w == 2 ? sx2 : sw0));
-        static_assert(kWStageBytes <= kXStageBytes, "pass size bounded by the smaller stage");
-        static_assert(3 * (kXStageBytes + kWStageBytes) <= 160 * 1024, "LDS of one CU");
+        auto slot = [&](int v, int f) __attribute__((always_inline)) {
+            uint8_t *base;
+            if (f < 8)
+                base = (v < 4 ? sx0 : sx1) + (v & 3) * 8192 + f * 1024;
+            else if (f < 16)
+                base = v < 4 ? sx2 + v * 8192 + (f - 8) * 1024
+                             : (v < 6 ? sw0 : sw1) + (v & 1) * (kKeep - 8 < 8 ? kKeep - 8 : 8) * 1024 + (f - 8) * 1024;
+            else
+                base = sw2 + v * 2048 + (f - 16) * 1024;
+            return reinterpret_cast<floatx4_t *>(base) + lane;
+        };
+        const bool upper = kh != 0;
 #pragma unroll
-        for (int p0 = 0; p0 < kAcc; p0 += kPass) {
-            if (kh == 1) {
+        for (int j = 0; j < Q; ++j)
 #pragma unroll
-                for (int f = p0; f < kAcc && f < p0 + kPass; ++f)
-                    red[(f - p0) * 64 + lane] = f < 8 * Q ? accF[f >> 3][f & 7] : accR[(f - 8 * Q) / RR][(f - 8 * Q) % RR];
+            for (int ii = 0; ii < 4; ++ii) {
+                const floatx4_t lo = accF[j][ii], hi = accF[j][ii + 4];
+                *slot(wave, 4 * j + ii) = upper ? lo : hi;
+                keep[4 * j + ii] = upper ? hi : lo;
             }
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            __builtin_amdgcn_s_barrier();
-            if (kh == 0) {
 #pragma unroll
-                for (int f = p0; f < kAcc && f < p0 + kPass; ++f) {
-                    if (f < 8 * Q)
-                        accF[f >> 3][f & 7] += red[(f - p0) * 64 + lane];
-                    else
-                        accR[(f - 8 * Q) / RR][(f - 8 * Q) % RR] += red[(f - p0) * 64 + lane];
-                }
+        for (int j = 0; j < RB; ++j)
+#pragma unroll
+            for (int ii = 0; ii < HR; ++ii) {
+                const floatx4_t lo = accR[j][ii], hi = accR[j][ii + HR];
+                *slot(wave, 4 * Q + HR * j + ii) = upper ? lo : hi;
+                keep[4 * Q + HR * j + ii] = upper ? hi : lo;
             }
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            __builtin_amdgcn_s_barrier();
-        }
-        if (kh == 1)
-            return;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
+#pragma unroll
+        for (int f = 0; f < kKeep; ++f)
+            keep[f] += *slot(wave ^ 4, f);
     }
+    // fragment f of keep: tile and 16-row block (wave-uniform)
+    auto frag_tile = [&](int f) __attribute__((always_inline)) {
+        return f < 4 * Q ? tile0 + w * Q + f / 4
+                         : tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + (f - 4 * Q) / (HR > 0 ? HR : 1));
+    };
+    auto frag_block = [&](int f) __attribute__((always_inline)) {
+        return f < 4 * Q ? (4 * kh + f % 4) ^ rb : rb + HR * kh + (f - 4 * Q) % (HR > 0 ? HR : 1);
+    };
 
     // ---- epilogue: lane (r, gq) holds rows 4*gq + i of each 16-row block ----
     if (SILU) {
+        const bool hi = r >= 8;
         if (buf_out) {
             // bf16 h through buffer stores as y below (2 bytes per output, rows
             // past M dropped at the buffer's end)
             const uint32_t hstride = (uint32_t)ldy * 2u;        // bytes per row of h
             const __amdgpu_buffer_rsrc_t hrs = make_rsrc(out, (uint32_t)M * hstride);
-            const bool hi = r >= 8;
             // lanes r < 8 write rows 4gq, 4gq+1 of a block, lanes r >= 8 rows
             // 4gq+2, 4gq+3; output f = 8t + r%8
             const uint32_t lane_row = (uint32_t)(4 * gq + (hi ? 2 : 0)) * hstride;
-            // tile t, block rows starting at the wave-uniform mrow; called with
-            // the wave's lanes all active
-            auto put = [&](int t, int mrow, const floatx4_t &v) __attribute__((always_inline)) {
-                const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-                const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
-                const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
-                const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
-                const uint32_t f = 8u * (uint32_t)t + (uint32_t)(r & 7);
-                const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)mrow * hstride));
-                const uint32_t off = lane_row + f * 2u + row;
-                __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * ga, g * ua), hrs, (int)off, 0, 0);
-                __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * gb, g * ub), hrs,
-                                                      (int)(off + hstride), 0, 0);
-            };
 #pragma unroll
-            for (int j = 0; j < Q; ++j) {
-                const int t = tile0 + w * Q + j;
+            for (int f = 0; f < kKeep; ++f) {
+                const int t = frag_tile(f);
                 if (t < NT) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        put(t, m0 + 16 * (i ^ rb), accF[j][i]);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < RB; ++j) {
-                const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
-                if (t < NT) {
-#pragma unroll
-                    for (int i = 0; i < RR; ++i)
-                        put(t, m0 + 16 * (rb + i), accR[j][i]);
+                    const floatx4_t v = keep[f];
+                    const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+                    const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
+                    const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
+                    const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
+                    const uint32_t fo = 8u * (uint32_t)t + (uint32_t)(r & 7);
+                    const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(
+                        (int)((uint32_t)(m0 + 16 * frag_block(f)) * hstride));
+                    const uint32_t off = lane_row + fo * 2u + row;
+                    __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * ga, g * ua), hrs, (int)off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * gb, g * ub), hrs,
+                                                          (int)(off + hstride), 0, 0);
                 }
             }
         } else {
             // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
             uint16_t *h = static_cast<uint16_t *>(out);
-            const bool hi = r >= 8;
-            // tile t, rows mrow + 0..3 (mrow = m0 + 16*block + 4*gq): outputs
-            // f = 8t + r%8; called with the wave's lanes all active
-            auto put = [&](int t, int mrow, const floatx4_t &v) __attribute__((always_inline)) {
-                const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-                const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
-                const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
-                const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
-                const int m = mrow + (hi ? 2 : 0);
-                const int64_t f = 8 * (int64_t)t + (r & 7);
-                if (m < M)
-                    h[(int64_t)m * ldy + f] = silu_mul_bf16(g * ga, g * ua);
-                if (m + 1 < M)
-                    h[(int64_t)(m + 1) * ldy + f] = silu_mul_bf16(g * gb, g * ub);
-            };
 #pragma unroll
-            for (int j = 0; j < Q; ++j) {
-                const int t = tile0 + w * Q + j;
+            for (int f = 0; f < kKeep; ++f) {
+                const int t = frag_tile(f);
                 if (t < NT) {
-#pragma unroll
-                    for (int i = 0; i < 8; ++i)
-                        put(t, m0 + 16 * (i ^ rb) + 4 * gq, accF[j][i]);
-                }
-            }
-#pragma unroll
-            for (int j = 0; j < RB; ++j) {
-                const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
-                if (t < NT) {
-#pragma unroll
-                    for (int i = 0; i < RR; ++i)
-                        put(t, m0 + 16 * (rb + i) + 4 * gq, accR[j][i]);
+                    const floatx4_t v = keep[f];
+                    const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+                    const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
+                    const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
+                    const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
+                    const int m = m0 + 16 * frag_block(f) + 4 * gq + (hi ? 2 : 0);
+                    const int64_t fo = 8 * (int64_t)t + (r & 7);
+                    if (m < M)
+                        h[(int64_t)m * ldy + fo] = silu_mul_bf16(g * ga, g * ua);
+                    if (m + 1 < M)
+                        h[(int64_t)(m + 1) * ldy + fo] = silu_mul_bf16(g * gb, g * ub);
                 }
             }
         }
@@ -482,35 +482,18 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         const uint32_t rstride = (uint32_t)ldy * 4u;            // bytes per row of y
         const __amdgpu_buffer_rsrc_t yrs = make_rsrc(out, (uint32_t)M * rstride);
         const uint32_t lane_row = (uint32_t)(4 * gq) * rstride;
-        auto put_y = [&](int n, int mrow, float v) __attribute__((always_inline)) {
-            // mrow: the wave-uniform part of the row (the lane adds 4gq)
-            const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)mrow * rstride));
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g * v), yrs,
-                                                  (int)(lane_row + (uint32_t)n * 4u + row), 0, 0);
-        };
 #pragma unroll
-        for (int j = 0; j < Q; ++j) {
-            const int t = tile0 + w * Q + j;
+        for (int f = 0; f < kKeep; ++f) {
+            const int t = frag_tile(f);
             const int n = t * 16 + r;
             if (t < NT && n < N) {
+                const int mb = m0 + 16 * frag_block(f);
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        put_y(n, m0 + 16 * (i ^ rb) + e, accF[j][i][e]);
+                for (int e = 0; e < 4; ++e) {
+                    const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(mb + e) * rstride));
+                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g * keep[f][e]), yrs,
+                                                          (int)(lane_row + (uint32_t)n * 4u + row), 0, 0);
                 }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < RB; ++j) {
-            const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
-            const int n = t * 16 + r;
-            if (t < NT && n < N) {
-#pragma unroll
-                for (int i = 0; i < RR; ++i)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        put_y(n, m0 + 16 * (rb + i) + e, accR[j][i][e]);
             }
         }
         return;
@@ -518,35 +501,17 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
     float *y = static_cast<float *>(out);
 #pragma unroll
-    for (int j = 0; j < Q; ++j) {
-        const int t = tile0 + w * Q + j;
+    for (int f = 0; f < kKeep; ++f) {
+        const int t = frag_tile(f);
         const int n = t * 16 + r;
         if (t < NT && n < N) {
+            const int mb = m0 + 16 * frag_block(f) + 4 * gq;
 #pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                const int mt = i ^ rb;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = m0 + 16 * mt + 4 * gq + e;
-                    if (m < M)
-                        y[(int64_t)m * ldy + n] = g * accF[j][i][e];
-                }
+            for (int e = 0; e < 4; ++e) {
+                const int m = mb + e;
+                if (m < M)
+                    y[(int64_t)m * ldy + n] = g * keep[f][e];
             }
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < RB; ++j) {
-        const int t = tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + j);
-        const int n = t * 16 + r;
-        if (t < NT && n < N) {
-#pragma unroll
-            for (int i = 0; i < RR; ++i)
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int m = m0 + 16 * (rb + i) + 4 * gq + e;
-                    if (m < M)
-                        y[(int64_t)m * ldy + n] = g * accR[j][i][e];
-                }
         }
     }
 }
