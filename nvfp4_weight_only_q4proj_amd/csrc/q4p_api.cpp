@@ -161,7 +161,8 @@ q4proj_status q4proj_pack_gate_up(const uint8_t *gate_codes, const uint8_t *gate
 {
     if (!gate_codes || !gate_scales || !up_codes || !up_scales || !packed_codes || !packed_scales)
         return Q4P_EINVAL;
-    if (F < 8 || F % 8 != 0 || !shape_ok(2 * F, K))
+    // F is bounded before 2F is formed (no signed overflow for any F)
+    if (F < 8 || F % 8 != 0 || F > ((int64_t)1 << 29) || !shape_ok(2 * F, K))
         return Q4P_EINVAL;
     // one global scale multiplies the fused projection: both halves need the
     // same one (bit for bit; a NaN never equals itself)

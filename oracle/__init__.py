@@ -34,17 +34,39 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "oracle.c")
-LIB = os.path.join(_HERE, "liboracle.so")
+LIB_PLAIN = os.path.join(_HERE, "liboracle.so")
+#: The same source built with AddressSanitizer and UndefinedBehaviorSanitizer
+#: (errors fatal).  Loading it needs the ASan runtime preloaded into the
+#: process; the CPU test of the sanitizer leg starts such processes.
+LIB_SAN = os.path.join(_HERE, "liboracle_san.so")
+#: Set to 1 in the environment to load (and build mutants as) the sanitized
+#: library.
+SANITIZE_ENV = "Q4P_SANITIZED_ORACLE"
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+
+
+def sanitized() -> bool:
+    return os.environ.get(SANITIZE_ENV) == "1"
+
+
+LIB = LIB_SAN if sanitized() else LIB_PLAIN
 
 #: Tolerance factor of the acceptance test: |y - y_ref| <= RTOL * sum_k |x_k w_k|.
 RTOL = 2e-3
 
 
-def build(src: str = SRC, out: str = LIB) -> str:
-    """Compile the oracle with gcc (plain C11, -O2, IEEE semantics kept)."""
+def build(src: str = SRC, out: str = LIB, sanitize: bool | None = None) -> str:
+    """Compile the oracle with gcc (plain C11, -O2, IEEE semantics kept);
+    with ``sanitize`` (default: the environment switch) under ASan and UBSan.
+    The sanitizers change no floating-point semantics."""
+    if sanitize is None:
+        sanitize = sanitized()
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-o", out, src, "-lm",
-           "-lpthread"]
+           "-ffp-contract=off", "-Wall", "-Wextra"]
+    if sanitize:
+        cmd += SANITIZE_FLAGS
+    cmd += ["-o", out, src, "-lm", "-lpthread"]
     subprocess.run(cmd, check=True)
     return out
 

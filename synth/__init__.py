@@ -30,7 +30,14 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 SRC = os.path.join(_HERE, "synth.c")
-LIB = os.path.join(_HERE, "libsynth.so")
+LIB_PLAIN = os.path.join(_HERE, "libsynth.so")
+#: The same source under AddressSanitizer and UndefinedBehaviorSanitizer,
+#: loaded instead of the plain library when the oracle's sanitizer switch
+#: (Q4P_SANITIZED_ORACLE=1) is set; the ASan runtime must be preloaded.
+LIB_SAN = os.path.join(_HERE, "libsynth_san.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all",
+                  "-fno-omit-frame-pointer", "-g"]
+LIB = LIB_SAN if os.environ.get("Q4P_SANITIZED_ORACLE") == "1" else LIB_PLAIN
 
 # stream ids
 STREAM_X = 100        # + matrix index
@@ -41,9 +48,12 @@ STREAM_C0_SCALES = 301
 WEIGHT_STD = 0.02
 
 
-def build(src: str = SRC, out: str = LIB) -> str:
+def build(src: str = SRC, out: str = LIB, sanitize: bool = False) -> str:
     cmd = ["gcc", "-std=c11", "-O2", "-fPIC", "-shared", "-fno-fast-math",
-           "-ffp-contract=off", "-Wall", "-Wextra", "-o", out, src, "-lm"]
+           "-ffp-contract=off", "-Wall", "-Wextra"]
+    if sanitize or out == LIB_SAN:
+        cmd += SANITIZE_FLAGS
+    cmd += ["-o", out, src, "-lm"]
     subprocess.run(cmd, check=True)
     return out
 
