@@ -20,6 +20,9 @@ Also measured and reported in the same JSON line:
                 `traffic` (HBM bytes per launch, mean of the two) from the
                 rocprofv3 counter summary in profiles/ when current.
   shapes        the other workloads' GEMVs (M = 7 verify, lm-head, 4B shapes).
+  verify_sweep  the speculative-verify GEMV over M = 1..16 rows for both MLP
+                matrices (gate/up 5120->17408, down 17408->5120): GB/s and the
+                fraction of 8 TB/s per M.
   fused_gate_up the MLP's gate and up weights as one fused 2F x K NVFP4
                 projection with the silu(gate)*up epilogue (bf16 out), F = 17408,
                 K = 5120: the GEMV at M = 1 and M = 7 and the GEMM at M = 512,
@@ -37,8 +40,9 @@ Also measured and reported in the same JSON line:
                 launch path a serving loop would use).
   cpu_baseline  the CPU oracle on the decode step, on the host cores, and on
                 one thread for the tiny case, the decode step and the 4B pair.
-  device_state_before_timing  clock levels and the processes holding a GPU
-                (idle check), from sysfs.
+  device_state_before_timing  clock levels (sysfs) and the processes holding
+                a GPU (amdsmi, in this process; idle check).
+  host          os.cpu_count(), the CPUs this process may run on, OMP_NUM_THREADS.
 """
 from __future__ import annotations
 
@@ -158,12 +162,35 @@ def device_state():
             state["clocks"][os.path.basename(os.path.dirname(card))] = levels
         except (OSError, IndexError):
             continue
-    try:
-        state["gpu_pids"] = sorted(int(p) for p in os.listdir("/sys/class/kfd/kfd/proc")
-                                   if p.isdigit() and int(p) != os.getpid())
-    except OSError:
-        pass
+    state["gpu_pids"], state["gpu_processes_source"] = gpu_processes()
     return state
+
+
+def gpu_processes():
+    """(pids of the other processes that hold a GPU, where the list came
+    from): amdsmi's per-GPU process list, read in this process before it
+    touches the GPU; the kfd sysfs directory when amdsmi is unusable."""
+    me = os.getpid()
+    try:
+        import amdsmi
+        amdsmi.amdsmi_init()
+        try:
+            pids = set()
+            for h in amdsmi.amdsmi_get_processor_handles():
+                for proc in amdsmi.amdsmi_get_gpu_process_list(h):
+                    pid = proc.get("pid") if isinstance(proc, dict) else None
+                    if isinstance(pid, int) and pid != me:
+                        pids.add(pid)
+            return sorted(pids), "amdsmi"
+        finally:
+            amdsmi.amdsmi_shut_down()
+    except Exception as e:  # noqa: BLE001 - any amdsmi failure falls back
+        err = f"amdsmi: {type(e).__name__}: {e}"[:200]
+    try:
+        return sorted(int(p) for p in os.listdir("/sys/class/kfd/kfd/proc")
+                      if p.isdigit() and int(p) != me), "kfd sysfs"
+    except OSError:
+        return None, err + "; no kfd sysfs process list"
 
 
 def graph_replay(torch, launches, steps_per_pass, passes):
@@ -199,7 +226,8 @@ def main():
     ap.add_argument("--skip-cpu", action="store_true", help="omit the cpu_baseline leg")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="wall-time bound of the cpu_baseline sample")
-    ap.add_argument("--only", choices=["dec", "pre", "shapes", "mlp", "argmax", "quant", "all"],
+    ap.add_argument("--only", choices=["dec", "pre", "shapes", "verify", "mlp", "argmax", "quant",
+                                       "all"],
                     default="all",
                     help="restrict the run (for profiling one kernel)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -243,7 +271,9 @@ def main():
         pc, ps = u["w"][i % len(u["w"])]
         return lambda: fn(pc, ps, u["g"], u["x"], u["y"], c.M, c.N, c.K)
 
-    out = {"metric": METRIC, "device_state_before_timing": smi}
+    out = {"metric": METRIC, "device_state_before_timing": smi,
+           "host": {"cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
+                    "omp_num_threads": os.environ.get("OMP_NUM_THREADS")}}
 
     # ---- decode step: gate/up + down GEMV at M = 1 -------------------------
     dec = synth.workload_cases("dec")
@@ -375,6 +405,40 @@ def main():
         out["pack"] = {"N": lm.N, "K": lm.K, "us": round(ms * 1e3, 1),
                        "gbs": round(moved / (ms * 1e-3) / 1e9, 1)}
         del codes, scales, pc, ps
+
+    # ---- speculative verify: M = 1..16 rows at once ------------------------
+    if args.only in ("verify", "all"):
+        sweep = {}
+        for c in synth.workload_cases("mtp"):
+            N, K = c.N, c.K
+            u = upload(c, copies_for(algo_bytes(16, N, K)))
+            ys = {}
+            per_m = {}
+            n = max(10, args.steps // 8)
+            for M in range(1, 17):
+                xm = torch.from_numpy(synth.x_bf16(7, 40 + M, M, K).view(np.int16)).to(dev)
+                ym = torch.empty((M, N), dtype=torch.float32, device=dev)
+                ys[M] = (xm, ym)
+
+                def vlaunch(i, M=M, xm=xm, ym=ym):
+                    pc, ps = u["w"][i % len(u["w"])]
+                    return lambda: q4.q4proj_gemv(pc, ps, u["g"], xm, ym, M, N, K)
+
+                for i in range(3):
+                    vlaunch(i)()
+                ms, _ = timed_region(torch, [vlaunch(i) for i in range(n)], n)
+                b = algo_bytes(M, N, K)
+                per_m[M] = {"us": round(ms * 1e3, 2), "gbs": round(b / (ms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+            sweep[f"{c.name} {K}->{N}"] = per_m
+            del u, ys
+        out["verify_sweep"] = {
+            "workload": "speculative verify: M = 1..16 activation rows through the NVFP4 GEMV "
+                        "(MLP gate/up 5120->17408 and down 17408->5120)",
+            "kernel": "gemv_sk_kernel<ceil(M/4), 4, KR, 0> (KR: joined k-ranges)",
+            "roofline": {"bound": "hbm", "peak": HBM_PEAK_GBS, "unit": "GB/s"},
+            "per_matrix": sweep, "launches_per_M": max(10, args.steps // 8),
+            "kernel_source_sha256_16": src_digest("q4p_gemv.hip")}
 
     # ---- fused gate/up + silu(gate)*up ------------------------------------
     if args.only in ("mlp", "all"):
@@ -530,6 +594,9 @@ def main():
                 break
         out["cpu_baseline"] = {"value": round(step_bytes * reps / el / 1e9, 3), "unit": "GB/s",
                                "cores": nthreads, "kind": "oracle",
+                               "host_cpu_count": os.cpu_count(),
+                               "threads_rule": "one oracle thread per CPU this process may run "
+                                               "on (its affinity mask), not os.cpu_count()",
                                "sample": f"{reps} full decode steps (gate/up + down, M=1, "
                                          f"all rows) in {el:.2f} s, fp64",
                                "tokens_per_s": round(reps / el, 2),
