@@ -396,18 +396,25 @@ gemv_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
 // commutative, so the result does not depend on which side comes second --
 // stores y and clears the word for the next call.  No fences, no waiting.
 //
-// When the activations of all of K do not fit, K is cut into KS ranges (a
-// power of two) that do, each streamed as above by its own G/KS workgroups.
-// The KS partial results of an output are then joined along a fixed binary
-// tree of the same two-party exchanges (ranges 2i and 2i+1 first, then pairs
-// of pairs, ...): each join adds two values, so the total does not depend on
+// K may be cut into KS ranges (a power of two), each streamed as above by
+// its own G/KS workgroups, which then stage only their range's activations.
+// The KS partial results of an output are joined along a fixed binary tree of
+// the same two-party exchanges (ranges 2i and 2i+1 first, then pairs of
+// pairs, ...): each join adds two values, so the total does not depend on
 // arrival order either.  The tree's words follow the boundary words in the
-// workspace, one per output and join.
+// workspace, one per output and join.  When a lane holds two or more rows of
+// a column (M > 4) it exchanges two rows per word, with the NaN-keyed pair
+// encoding below, both between workgroups and up the tree, so the side that
+// completes one row completes its partner row too.  KS trades staging (every
+// workgroup reads its range's activations into LDS) against joining; the
+// launcher picks the count with the least measured cost (sk_ranges).
 
 constexpr int kSkMaxGroups = 256;
 constexpr int kSkMaxWaves = 8;
 constexpr int kSkPrefetch = 4;
-constexpr int kSkXMaxBytes = 128 * 1024;       // + 16 KB of partial sums stays within 160 KB
+// activations of a range in LDS: all of a CU's 160 KB beside the zero strip
+// and the partial sums of 8 waves (2 x 1 KB each)
+constexpr int kSkXMaxBytes = 160 * 1024 - kZeroBytes - kSkMaxWaves * 2 * 64 * 16;
 constexpr int kSkLdsFloor = 96 * 1024;
 // 16-byte activation loads per lane issued together before the ring (the
 // rest follow one at a time): 8 when M <= 4, 16 above, where the activations
@@ -718,6 +725,38 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
             bestk[j] = k > bestk[j] ? k : bestk[j];
         }
     };
+    // Two rows m, m + 1 of output column col held by one lane (ROWS >= 2):
+    // the same tree with both values in one word (pair_word, never zero), so
+    // each join level costs one exchange per two outputs.  The word of row
+    // m is used; row m + 1's stays zero.  Row m + 1 may lie past M (its value
+    // is then never stored).
+    auto join2 = [&](int m, int col, float v0, float v1, int j) {
+        for (int span = 1; span < (KR ? a.KS : 1); span *= 2) {
+            const int set = (a.KS - a.KS / span) + kr / (2 * span);
+            unsigned long long *wd = xch + kSkBoundaryWords + ((int64_t)set * M + m) * N + col;
+            const unsigned long long old = __hip_atomic_exchange(
+                wd, pair_word(v0, v1), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if (old == 0ull)
+                return;                                 // the partner side goes on
+            v0 = pair_gate(old) + v0;
+            v1 = pair_up(old) + v1;
+            __hip_atomic_store(wd, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        const float g0 = g * v0, g1 = g * v1;
+        if (!ARGMAX || y != nullptr) {
+            y[(int64_t)m * N + col] = g0;
+            if (m + 1 < M)
+                y[(int64_t)(m + 1) * N + col] = g1;
+        }
+        if (ARGMAX) {
+            const unsigned long long k0 = argmax_key(g0, col);
+            bestk[j] = k0 > bestk[j] ? k0 : bestk[j];
+            if (m + 1 < M) {
+                const unsigned long long k1 = argmax_key(g1, col);
+                bestk[j + 1] = k1 > bestk[j + 1] ? k1 : bestk[j + 1];
+            }
+        }
+    };
     // SILU: the same for this range's complete gate and up values of output
     // (m, f), one word per pair; the last join applies the epilogue
     auto join_pair = [&](int m, int f, float vg, float vu) {
@@ -755,11 +794,16 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
         const int col = 16 * tt + r;
         if (col < N) {
 #pragma unroll
-            for (int j = 0; j < ROWS; ++j) {
+            for (int j = 0; j < ROWS; j += 2) {
                 const int m = out_row(gq, j);
                 const float vj = v[j];
-                if (m < M)
+                if (j + 1 < ROWS) {
+                    const float vk = v[j + 1];
+                    if (m < M)
+                        join2(m, col, vj, vk, j);
+                } else if (m < M) {
                     join(m, col, vj, j);
+                }
             }
         }
     };
@@ -893,12 +937,24 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
         }
         const int col = 16 * tau + r;
 #pragma unroll
-        for (int j = 0; j < ROWS; ++j) {
+        for (int j = 0; j < ROWS; j += 2) {
             const int m = out_row(gq, j);
             if (m < M) {
-                // copy the element out first: clang mis-lowers a bit_cast whose
+                // copy the elements out first: clang mis-lowers a bit_cast whose
                 // operand is a vector element (it reads element 0)
                 const float sj = sum[j];
+                if (j + 1 < ROWS) {
+                    // rows m, m + 1 in one word (slot j; slot j + 1 unused)
+                    const float sk = sum[j + 1];
+                    const unsigned long long old = __hip_atomic_exchange(
+                        slot + j, pair_word(sj, sk), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    if (old != 0ull) {
+                        __hip_atomic_store(slot + j, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                        if (col < N)
+                            join2(m, col, pair_gate(old) + sj, pair_up(old) + sk, j);
+                    }
+                    continue;
+                }
                 const unsigned long long mine =
                     (1ull << 32) | (unsigned long long)__builtin_bit_cast(uint32_t, sj);
                 const unsigned long long old = __hip_atomic_exchange(
@@ -1097,25 +1153,65 @@ gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges, int epi)
     }
 }
 
-// K ranges for the stream-K kernel: the fewest (a power of two) whose
-// activations fit in LDS.
-int64_t sk_ranges(int64_t M, int64_t K)
+// Exchange words one join level touches per output column: a lane holds
+// rows ROWS*gq + j (j < ROWS) of a column and joins them two to a word when
+// ROWS >= 2 (one per row when ROWS = 1); the fused gate/up epilogue joins
+// (gate, up) pairs, one word per output f.
+int64_t sk_join_words_per_col(int64_t M, bool silu)
 {
-    const int64_t KT = k_tiles(K);
-    int64_t KS = 1;
-    while (KS < kSkMaxRanges && M * ((KT + KS - 1) / KS) * 256 > kSkXMaxBytes)
-        KS *= 2;
-    return KS;
+    if (silu)
+        return M;
+    const int64_t rows = (M + 3) / 4;                   // ROWS
+    int64_t w = 0;
+    for (int64_t gq = 0; gq < 4; ++gq)
+        for (int64_t j = 0; j < rows; j += rows >= 2 ? 2 : 1)
+            w += rows * gq + j < M ? 1 : 0;
+    return w;
 }
 
-// The stream-K kernel serves a shape when its ranges' activations fit in LDS,
-// every range gets at least one k-tile, and the packed codes stay below
-// 4 GiB (32-bit buffer offsets: fewer than 2^22 units of 1 KB).
-bool sk_usable(int64_t M, int64_t N, int64_t K)
+// K ranges for the stream-K kernel (a power of two, 0 when none fits).  One
+// range stages the activations of all of K in every workgroup; more ranges
+// stage less each but join their partial sums through the workspace.  The
+// count with the least estimated cost is used, from timings of the verify
+// shapes on MI355X: staging about 22 ns per KB per workgroup, joining about
+// 14 ns per 1000 exchange words, and about 0.6 us per level of the join
+// tree.  Columns: N outputs (F for the fused gate/up epilogue).
+constexpr double kSkStageUsPerKB = 0.0224;
+constexpr double kSkJoinUsPerKWord = 0.0137;
+constexpr double kSkLevelUs = 0.6;
+
+int64_t sk_ranges(int64_t M, int64_t N, int64_t K, bool silu)
 {
-    const int64_t KT = k_tiles(K), NT = n_tiles(N), KS = sk_ranges(M, K);
-    const int64_t KTR = (KT + KS - 1) / KS;
-    return M * KTR * 256 <= kSkXMaxBytes && KT - (KS - 1) * KTR >= 1 && NT * KT < ((int64_t)1 << 22);
+    const int64_t KT = k_tiles(K);
+    const int64_t cols = silu ? N / 2 : N;
+    const int64_t wpc = sk_join_words_per_col(M, silu);
+    int64_t best = 0;
+    double best_cost = 0.0;
+    int level = 0;
+    for (int64_t KS = 1; KS <= kSkMaxRanges; KS *= 2, ++level) {
+        const int64_t KTR = (KT + KS - 1) / KS;
+        if (KT - (KS - 1) * KTR < 1)
+            break;                                      // a range without k-tiles
+        const int64_t xbytes = M * KTR * 256;
+        if (xbytes > kSkXMaxBytes)
+            continue;
+        const double cost = kSkStageUsPerKB * (double)xbytes / 1024.0 +
+                            kSkJoinUsPerKWord * (double)((KS - 1) * wpc * cols) / 1000.0 +
+                            kSkLevelUs * level;
+        if (best == 0 || cost < best_cost) {
+            best = KS;
+            best_cost = cost;
+        }
+    }
+    return best;
+}
+
+// The stream-K kernel serves a shape when some K range count fits its
+// activations in LDS, and the packed codes stay below 4 GiB (32-bit buffer
+// offsets: fewer than 2^22 units of 1 KB).
+bool sk_usable(int64_t M, int64_t N, int64_t K, bool silu)
+{
+    return sk_ranges(M, N, K, silu) > 0 && n_tiles(N) * k_tiles(K) < ((int64_t)1 << 22);
 }
 
 struct SkPlan {
@@ -1130,7 +1226,7 @@ struct SkPlan {
 SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, int epi)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
-    const int64_t KS = sk_ranges(M, K);
+    const int64_t KS = sk_ranges(M, N, K, epi == kEpiSilu);
     const int64_t KTR = (KT + KS - 1) / KS;
     int64_t GR = device_cus() / KS;                     // workgroups per K range
     if (GR > kSkMaxGroups / KS)
@@ -1184,20 +1280,20 @@ size_t gemv_workspace_bytes(int64_t M, int64_t N, int64_t K)
 {
     if (M < 1 || M > 16 || N < 1 || K < 1)
         return 0;
-    const int64_t KS = sk_usable(M, N, K) ? sk_ranges(M, K) : 1;
+    const int64_t KS = sk_usable(M, N, K, false) ? sk_ranges(M, N, K, false) : 1;
     return (size_t)(kSkBoundaryWords + (KS - 1) * M * N) * sizeof(unsigned long long);
 }
 
 bool gemv_silu_mul_supported(int64_t M, int64_t F, int64_t K)
 {
-    return M >= 1 && M <= 16 && F >= 8 && F % 8 == 0 && K >= 1 && sk_usable(M, 2 * F, K);
+    return M >= 1 && M <= 16 && F >= 8 && F % 8 == 0 && K >= 1 && sk_usable(M, 2 * F, K, true);
 }
 
 size_t gemv_silu_mul_workspace_bytes(int64_t M, int64_t F, int64_t K)
 {
     if (!gemv_silu_mul_supported(M, F, K))
         return 0;
-    const int64_t KS = sk_ranges(M, K);
+    const int64_t KS = sk_ranges(M, 2 * F, K, true);
     return (size_t)(kSkBoundaryWords + (KS - 1) * M * F) * sizeof(unsigned long long);
 }
 
@@ -1206,7 +1302,7 @@ hipError_t launch_gemv(const uint8_t *packed_codes, const uint8_t *packed_scales
                        void *workspace, hipStream_t stream)
 {
     const int64_t KT = k_tiles(K), NT = n_tiles(N);
-    if (sk_usable(M, N, K)) {
+    if (sk_usable(M, N, K, false)) {
         const SkPlan p = cached_sk_plan(M, N, K, kEpiY);
         SkArgs args = p.args;
         args.g = g;
@@ -1242,7 +1338,7 @@ hipError_t launch_gemv_silu_mul(const uint8_t *packed_codes, const uint8_t *pack
 
 bool gemv_argmax_supported(int64_t M, int64_t N, int64_t K)
 {
-    return M >= 1 && M <= 16 && N >= 1 && K >= 1 && sk_usable(M, N, K);
+    return M >= 1 && M <= 16 && N >= 1 && K >= 1 && sk_usable(M, N, K, false);
 }
 
 size_t gemv_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K)

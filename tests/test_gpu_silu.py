@@ -166,11 +166,12 @@ def test_nan_scale_poisons_its_pair():
 
 def test_rejects_what_it_does_not_serve():
     m = q4()
+    KBIG = 288 * 128
     # one buffer stands in for both packed weights: as large as the packed
     # codes of the largest shape below, so no output range overlaps it
-    w = torch.zeros(q4().q4proj_packed_codes_bytes(32, 32896), dtype=torch.uint8, device=DEV)
+    w = torch.zeros(q4().q4proj_packed_codes_bytes(32, KBIG), dtype=torch.uint8, device=DEV)
     ws = torch.zeros(1 << 20, dtype=torch.uint8, device=DEV)
-    x = torch.zeros(16 * 32896, dtype=torch.int16, device=DEV)
+    x = torch.zeros(16 * KBIG, dtype=torch.int16, device=DEV)
     h = torch.zeros(16 * 32, dtype=torch.int16, device=DEV)
     lib = m.library()
 
@@ -178,11 +179,19 @@ def test_rejects_what_it_does_not_serve():
         return lib.q4proj_gemv_silu_mul(w.data_ptr(), w.data_ptr(), 1.0, x.data_ptr(), h.data_ptr(),
                                         M, F, K, ws.data_ptr(), ws.numel(), None)
 
-    # F % 8 != 0, M > 16, K past the eight-range limit at M = 16: rejected
-    # on the host, nothing launched
+    # F % 8 != 0, M > 16, K past the eight-range limit at M = 16 (a range of
+    # 36 k-tiles of 16 activation rows needs 147456 bytes of LDS, more than
+    # the 147392 left beside the partial sums): rejected on the host, nothing
+    # launched
     assert call(1, 12, 128) == m.EINVAL
     assert call(17, 16, 128) == m.EUNSUPPORTED
-    assert call(16, 16, 32896) == m.EUNSUPPORTED
+    assert call(16, 16, KBIG) == m.EUNSUPPORTED
+    # the largest K served at M = 16: 35 k-tiles per range (143360 bytes);
+    # all-zero weights give h = 0
+    h.fill_(1)
+    assert call(16, 16, 280 * 128) == m.OK
+    torch.cuda.synchronize()
+    assert int(h[:16 * 16].count_nonzero()) == 0
 
 
 # ---- the matrix-core path (any M) ------------------------------------------
