@@ -97,14 +97,17 @@ RAGGED = {
     # (7, 4352, 640) .. (12, 5000, 3088) have more row tiles than a 256-CU
     # device has CUs and per-CU ranges that end inside row tiles: their split
     # row tiles are finished across workgroups, for every output row M can
-    # hold.  (7, 200, 17408) .. (16, 1000, 32768) cut K into 2, 4, 2 (ragged)
-    # and 8 ranges whose results are joined per output.  The last three need
-    # more than 8 ranges and run on the split kernel (activation pieces in
-    # the register ring): M > 8, M = 1 and M = 3.
+    # hold.  (16, 272, 2000), (12, 130, 9216) and (7, 200, 17408) ..
+    # (16, 1000, 32768) cut K into 2, 4, 8, 8, 2 (ragged) and 8 ranges
+    # (the launcher's cost estimate picks the count) whose results are
+    # joined per output, two rows per word above M = 4.  The last three need
+    # more than 8 ranges (a range's activations would not fit in LDS) and run
+    # on the split kernel (activation pieces in the register ring): M > 8,
+    # M = 1 and M = 3.
     "gemv": [(5, 1000, 1040), (16, 272, 2000), (1, 3, 4112), (7, 33, 144), (3, 4097, 128),
              (12, 130, 9216), (7, 4352, 640), (2, 6000, 272), (16, 4368, 912),
              (12, 5000, 3088), (7, 200, 17408), (16, 272, 16384), (9, 4352, 8320),
-             (16, 1000, 32768), (16, 300, 33024), (1, 100, 1048576), (3, 40, 200000)],
+             (16, 1000, 32768), (16, 300, 36864), (1, 100, 1048576), (3, 40, 200000)],
     "gemm": [(129, 300, 1040), (513, 100, 272), (1, 17, 5136), (200, 4112, 128),
              (64, 2049, 400), (300, 48, 2000)],
 }
@@ -123,9 +126,11 @@ def test_ragged_shapes(kind):
 def test_gemv_every_m(M):
     """Every M of the decode/verify range on two shapes: 4352 x 640 (272 row
     tiles over one workgroup per CU, so row tiles are split between waves and
-    between workgroups) and 300 x K with two K ranges (the activations of all
-    of K exceed one range's LDS).  Each M places its rows differently in the
-    lanes' output slots (two per lane up to M = 8, four above)."""
+    between workgroups) and 300 x K with K cut into ranges (four at these
+    sizes: the activations of all of K would not fit in LDS, and the joins
+    of 300 columns are cheap).  Each M places its rows differently in the
+    lanes' output slots (one per lane up to M = 4, two up to M = 8, three or
+    four above) and above M = 4 joins two rows per exchange word."""
     for j, (N, K) in enumerate([(4352, 640), (300, 128 * (512 // M + 4))]):
         m = synth.nvfp4_normal_matrix(60 + M, 3 + j, N, K)
         x = synth.x_bf16(60 + M, 4 + j, M, K)
