@@ -38,6 +38,8 @@ Also measured and reported in the same JSON line:
                 reads w for its max, the second reads it again to quantize.
   graph_replay  the decode step captured as a HIP graph and replayed (the
                 launch path a serving loop would use).
+  prepared_calls  the decode step through prepared launchers (host time per
+                launch without the binding's per-call checks).
   cpu_baseline  the CPU oracle on the decode step, on the host cores, and on
                 one thread for the tiny case, the decode step and the 4B pair.
   device_state_before_timing  clock levels (sysfs) and the processes holding
@@ -337,6 +339,18 @@ def main():
             "host_us_per_replay": round(g_host, 2),
             "note": "the decode step captured as a HIP graph (torch.cuda.CUDAGraph over the "
                     "C-ABI calls, caller-owned buffers, no allocation per call)"}
+        # the same launches through prepared calls: the binding's checks run
+        # once per (weight copy, matrix), each step only calls the C entry
+        prep = [[q4.prepare_gemv(pc, ps, u["g"], u["x"], u["y"], u["case"].M, u["case"].N,
+                                 u["case"].K) for (pc, ps) in u["w"]] for u in dec_u]
+        p_ms, p_host = timed_region(
+            torch, [prep[j][(args.warmup + i) % ncopy] for i in range(args.steps)
+                    for j in range(len(dec_u))], args.steps)
+        out["prepared_calls"] = {
+            "ms_per_step": round(p_ms, 5), "gbs": round(step_bytes / (p_ms * 1e-3) / 1e9, 1),
+            "host_enqueue_us_per_launch": round(p_host / (args.steps * len(dec_u)) * 1e6, 2),
+            "note": "the decode step through prepare_gemv launchers (arguments checked and "
+                    "converted once; the C ABI still validates every call)"}
 
     # ---- prefill chunk: M = 512 GEMM --------------------------------------
     if args.only in ("pre", "all"):

@@ -272,7 +272,10 @@ def _bf16_bits(t, name):
     return t
 
 
-def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, workspace, stream):
+def _proj_args(name, packed_codes, packed_scales, global_scale, x, y, M, N, K, workspace,
+               stream):
+    """Checks of a projection call; (device, the C arguments, the tensors they
+    point into)."""
     dev = _dev(x, "x")
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
@@ -280,15 +283,21 @@ def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, w
     _need(x, "x", x.dtype, M * K, dev)
     _need(y, "y", torch.float32, M * N, dev)
     ws_ptr, ws_bytes = None, 0
-    if workspace is None and fn is _lib.q4proj_gemv:
+    if workspace is None and name == "q4proj_gemv":
         workspace = default_workspace(dev, q4proj_workspace_bytes(M, N, K), stream)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    args = (packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale), x.data_ptr(),
+            y.data_ptr(), M, N, K, ws_ptr, ws_bytes, _stream(dev, stream))
+    return dev, args, (packed_codes, packed_scales, x, y, workspace)
+
+
+def _proj(fn, where, packed_codes, packed_scales, global_scale, x, y, M, N, K, workspace, stream):
+    dev, args, _ = _proj_args(where, packed_codes, packed_scales, global_scale, x, y, M, N, K,
+                              workspace, stream)
     with _guard(dev):
-        _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
-                  x.data_ptr(), y.data_ptr(), M, N, K, ws_ptr, ws_bytes, _stream(dev, stream)),
-               where)
+        _check(fn(*args), where)
 
 
 def q4proj_gemv(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,
@@ -336,8 +345,8 @@ def q4proj_gemm_silu_mul(packed_codes, packed_scales, global_scale: float, x, h,
               global_scale, x, h, M, F, K, workspace, stream)
 
 
-def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, K, workspace,
-              stream):
+def _silu_mul_args(name, packed_codes, packed_scales, global_scale, x, h, M, F, K, workspace,
+                   stream):
     dev = _dev(x, "x")
     N = 2 * F
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
@@ -347,15 +356,22 @@ def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, 
     _need(x, "x", x.dtype, M * K, dev)
     _need(h, "h", h.dtype, M * F, dev)
     ws_ptr, ws_bytes = None, 0
-    if workspace is None and fn is _lib.q4proj_gemv_silu_mul:
+    if workspace is None and name == "q4proj_gemv_silu_mul":
         workspace = default_workspace(dev, q4proj_silu_mul_workspace_bytes(M, F, K), stream)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
+    args = (packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale), x.data_ptr(),
+            h.data_ptr(), M, F, K, ws_ptr, ws_bytes, _stream(dev, stream))
+    return dev, args, (packed_codes, packed_scales, x, h, workspace)
+
+
+def _silu_mul(fn, where, packed_codes, packed_scales, global_scale, x, h, M, F, K, workspace,
+              stream):
+    dev, args, _ = _silu_mul_args(where, packed_codes, packed_scales, global_scale, x, h, M, F,
+                                  K, workspace, stream)
     with _guard(dev):
-        _check(fn(packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale),
-                  x.data_ptr(), h.data_ptr(), M, F, K, ws_ptr, ws_bytes, _stream(dev, stream)),
-               where)
+        _check(fn(*args), where)
 
 
 @functools.lru_cache(maxsize=4096)
@@ -367,6 +383,14 @@ def q4proj_gemv_argmax(packed_codes, packed_scales, global_scale: float, x, y, m
                        M: int, N: int, K: int, workspace=None, stream=None) -> None:
     """Greedy argmax of each row of the logits x . dequant(W)^T (1 <= M <= 16):
     max_val float32 [M], max_idx int64 [M]; y (fp32 [M][N]) may be None."""
+    dev, args, _ = _argmax_args(packed_codes, packed_scales, global_scale, x, y, max_val,
+                                max_idx, M, N, K, workspace, stream)
+    with _guard(dev):
+        _check(_lib.q4proj_gemv_argmax(*args), "q4proj_gemv_argmax")
+
+
+def _argmax_args(packed_codes, packed_scales, global_scale, x, y, max_val, max_idx, M, N, K,
+                 workspace, stream):
     dev = _dev(x, "x")
     _need(packed_codes, "packed_codes", torch.uint8, q4proj_packed_codes_bytes(N, K), dev)
     _need(packed_scales, "packed_scales", torch.uint8, q4proj_packed_scales_bytes(N, K), dev)
@@ -382,12 +406,100 @@ def q4proj_gemv_argmax(packed_codes, packed_scales, global_scale: float, x, y, m
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
         ws_ptr, ws_bytes = workspace.data_ptr(), workspace.numel()
-    with _guard(dev):
-        _check(_lib.q4proj_gemv_argmax(packed_codes.data_ptr(), packed_scales.data_ptr(),
-                                       float(global_scale), x.data_ptr(),
-                                       None if y is None else y.data_ptr(), max_val.data_ptr(),
-                                       max_idx.data_ptr(), M, N, K, ws_ptr, ws_bytes,
-                                       _stream(dev, stream)), "q4proj_gemv_argmax")
+    args = (packed_codes.data_ptr(), packed_scales.data_ptr(), float(global_scale), x.data_ptr(),
+            None if y is None else y.data_ptr(), max_val.data_ptr(), max_idx.data_ptr(), M, N, K,
+            ws_ptr, ws_bytes, _stream(dev, stream))
+    return dev, args, (packed_codes, packed_scales, x, y, max_val, max_idx, workspace)
+
+
+# ---- prepared calls ---------------------------------------------------------
+# A decode loop makes the same call on the same buffers every step.  The
+# prepare_* functions run the eager call's checks once and return a launcher
+# that goes straight to the C entry point with its arguments already
+# converted to C values: no per-call Python checks (the library still
+# validates every call on the host).
+_lib_raw = ctypes.CDLL(LIB_PATH)    # the same library, entry points without argtypes
+
+# C types of the eleven arguments shared by the projection entry points
+_PROJ_CTYPES = (_vp, _vp, _f32, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp)
+_ARGMAX_CTYPES = (_vp, _vp, _f32, _vp, _vp, _vp, _vp, _i64, _i64, _i64, _vp, _sz, _vp)
+
+
+class Prepared:
+    """One entry point bound to fixed buffers, sizes, workspace and stream
+    (the stream current at preparation when none was given).  Calling it
+    enqueues the call again.  It keeps the tensors it was prepared with
+    alive; they must keep their storage (no resize, no re-allocation).  The
+    device they live on is made current for the call when it is not."""
+
+    __slots__ = ("_fn", "_args", "_where", "_dev", "_keep")
+
+    def __init__(self, name, ctypes_seq, args, dev, keep):
+        self._fn = getattr(_lib_raw, name)
+        self._fn.restype = ctypes.c_int
+        self._args = tuple(t(a) for t, a in zip(ctypes_seq, args))
+        self._where = name
+        self._dev = dev
+        self._keep = keep
+
+    def __call__(self) -> None:
+        if _cur_device() == self._dev:
+            st = self._fn(*self._args)
+        else:
+            with torch.cuda.device(self._dev):
+                st = self._fn(*self._args)
+        if st != OK:
+            raise Q4ProjError(st, self._where)
+
+
+def prepare_gemv(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,
+                 workspace=None, stream=None) -> Prepared:
+    """q4proj_gemv bound to these buffers (see Prepared)."""
+    dev, args, keep = _proj_args("q4proj_gemv", packed_codes, packed_scales, global_scale, x, y,
+                                 M, N, K, workspace, stream)
+    return Prepared("q4proj_gemv", _PROJ_CTYPES, args, dev, keep)
+
+
+def prepare_gemm(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,
+                 workspace=None, stream=None) -> Prepared:
+    """q4proj_gemm bound to these buffers (see Prepared)."""
+    dev, args, keep = _proj_args("q4proj_gemm", packed_codes, packed_scales, global_scale, x, y,
+                                 M, N, K, workspace, stream)
+    return Prepared("q4proj_gemm", _PROJ_CTYPES, args, dev, keep)
+
+
+def prepare_gemv_silu_mul(packed_codes, packed_scales, global_scale: float, x, h, M: int, F: int,
+                          K: int, workspace=None, stream=None) -> Prepared:
+    """q4proj_gemv_silu_mul bound to these buffers (see Prepared)."""
+    dev, args, keep = _silu_mul_args("q4proj_gemv_silu_mul", packed_codes, packed_scales,
+                                     global_scale, x, h, M, F, K, workspace, stream)
+    return Prepared("q4proj_gemv_silu_mul", _PROJ_CTYPES, args, dev, keep)
+
+
+def prepare_gemm_silu_mul(packed_codes, packed_scales, global_scale: float, x, h, M: int, F: int,
+                          K: int, workspace=None, stream=None) -> Prepared:
+    """q4proj_gemm_silu_mul bound to these buffers (see Prepared)."""
+    dev, args, keep = _silu_mul_args("q4proj_gemm_silu_mul", packed_codes, packed_scales,
+                                     global_scale, x, h, M, F, K, workspace, stream)
+    return Prepared("q4proj_gemm_silu_mul", _PROJ_CTYPES, args, dev, keep)
+
+
+def prepare_gemv_noalloc(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int,
+                         K: int, stream=None) -> Prepared:
+    """q4proj_gemv_noalloc bound to these buffers (see Prepared)."""
+    dev, args, keep = _proj_args("q4proj_gemv_noalloc", packed_codes, packed_scales, global_scale,
+                                 x, y, M, N, K, None, stream)
+    noalloc_args = args[:8] + args[10:]                  # no workspace arguments
+    return Prepared("q4proj_gemv_noalloc", _PROJ_CTYPES[:8] + _PROJ_CTYPES[10:], noalloc_args,
+                    dev, keep)
+
+
+def prepare_gemv_argmax(packed_codes, packed_scales, global_scale: float, x, y, max_val, max_idx,
+                        M: int, N: int, K: int, workspace=None, stream=None) -> Prepared:
+    """q4proj_gemv_argmax bound to these buffers (see Prepared)."""
+    dev, args, keep = _argmax_args(packed_codes, packed_scales, global_scale, x, y, max_val,
+                                   max_idx, M, N, K, workspace, stream)
+    return Prepared("q4proj_gemv_argmax", _ARGMAX_CTYPES, args, dev, keep)
 
 
 def q4proj_quantize_workspace_bytes(N: int, K: int) -> int:
