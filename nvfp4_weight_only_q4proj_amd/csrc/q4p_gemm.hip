@@ -34,7 +34,8 @@
 //    Chunks are XOR-swizzled by row within LDS so the rows one read touches
 //    fall in different banks.  The matching eight weight codes are halves of
 //    two code slots of the packed tile (one byte permute); they share one
-//    e4m3 scale.
+//    e4m3 scale.  The code slots are XOR-swizzled within the weight stage
+//    too (code_pos), so the slots one read touches fall in different banks.
 //  * Software pipeline: a wave's operands for its second k-step are
 //    dequantised between the MFMAs of its first; one workgroup barrier per
 //    k-tile sits between the two steps (past it, stage c+1 has landed
@@ -101,6 +102,18 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t wd, float s)
     v.z = fp4x2_scaled_to_bf16x2<2>(wd, s);
     v.w = fp4x2_scaled_to_bf16x2<3>(wd, s);
     return __builtin_bit_cast(bf16x8_t, v);
+}
+
+// Position of code slot s (16 bytes) of a packed tile in a weight stage.
+// A k-step's read takes 8 bytes of slots 32h + r and 32h + r + 16 (r < 16,
+// h = 0, 1) in one ds_read2_b64, so without a swizzle the slots r, r + 8,
+// r + 32 and r + 40 of one half-wave share LDS banks.  XORing bit 3 into bit
+// 0 and bit 5 into bit 1 spreads them over different banks and leaves bit 4
+// alone, so the second slot stays 256 bytes after the first; the map is its
+// own inverse, so the stage loads fetch slot code_pos(p) into position p.
+__device__ __forceinline__ int code_pos(int s)
+{
+    return s ^ ((s >> 3) & 1) ^ (((s >> 5) & 1) << 1);
 }
 
 // gfx9 s_waitcnt immediates: vmcnt(0) (expcnt and lgkmcnt left alone) and
@@ -175,7 +188,9 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         const int e = 64 * (8 * q + wave) + lane;
         const bool code = 8 * q + wave < TT;
         const int j = code ? e >> 6 : (e - 64 * TT) >> 3;
-        const int part = code ? (e & 63) : ((e - 64 * TT) & 7);
+        // the lane filling stage position p of a code tile fetches slot
+        // code_pos(p), so slot s lands at position code_pos(s)
+        const int part = code ? code_pos(e & 63) : ((e - 64 * TT) & 7);
         const int t = tile0 + j;
         const int64_t tb = code ? kTileCodeBytes : kTileScaleBytes;
         woff[q] = t < NT && e < kWChunks ? (uint32_t)((int64_t)t * KT * tb + part * 16) : kOutside;
@@ -231,7 +246,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     // permute picks block 2d + gq/2 of each
     const int h = gq & 1;
     const uint32_t sel = (gq >> 1) ? 0x07060302u : 0x05040100u;
-    const int code_lane = (32 * h + r) * 16 + kh * 8;
+    const int code_lane = code_pos(32 * h + r) * 16 + kh * 8;
     const int scale_lane = r * 8 + kh * 4;
     const int a_lane = r * 256;
     // The wave visits row blocks i ^ rb, i = 0..7 (rb is even, a multiple of
