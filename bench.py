@@ -16,9 +16,12 @@ Also measured and reported in the same JSON line:
                 `traffic` from the rocprofv3 FETCH_SIZE/WRITE_SIZE summary in
                 profiles/ when it was taken on the current kernel source.
   prefill_gemm  the M = 512 prefill chunk (qkv 5120->14336, gate/up
-                5120->17408): TFLOP/s vs 2.517 PFLOP/s dense bf16; its
-                `traffic` (HBM bytes per launch, mean of the two) from the
-                rocprofv3 counter summary in profiles/ when current.
+                5120->17408) as the binding calls it (fp16 staging kernel +
+                GEMM on fp16 operands): TFLOP/s vs 2.517 PFLOP/s dense
+                bf16/fp16, with the time of the bf16-operand path (no
+                workspace) beside it; `traffic` (HBM bytes per GEMM launch,
+                mean of the two) from the rocprofv3 counter summary in
+                profiles/ when current.
   shapes        the other workloads' GEMVs (M = 7 verify, lm-head, 4B shapes).
   verify_sweep  the speculative-verify GEMV over M = 1..16 rows for both MLP
                 matrices (gate/up 5120->17408, down 17408->5120): GB/s and the
@@ -268,10 +271,15 @@ def main():
         return max(2, -(-MALL_DEFEAT_BYTES // step_bytes))
 
     def launcher(kind, u, i):
-        fn = q4.q4proj_gemv if kind == "gemv" else q4.q4proj_gemm
+        # "gemm": the binding's default, fp16 operands staged in its GEMM
+        # scratch (staging kernel + GEMM); "gemm_bf16": no workspace, bf16
+        # operands (one kernel)
         c = u["case"]
         pc, ps = u["w"][i % len(u["w"])]
-        return lambda: fn(pc, ps, u["g"], u["x"], u["y"], c.M, c.N, c.K)
+        if kind == "gemv":
+            return lambda: q4.q4proj_gemv(pc, ps, u["g"], u["x"], u["y"], c.M, c.N, c.K)
+        ws = False if kind == "gemm_bf16" else None
+        return lambda: q4.q4proj_gemm(pc, ps, u["g"], u["x"], u["y"], c.M, c.N, c.K, workspace=ws)
 
     out = {"metric": METRIC, "device_state_before_timing": smi,
            "host": {"cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0)),
@@ -361,24 +369,34 @@ def main():
         for i in range(max(3, args.warmup // 4)):
             for u in pre_u:
                 launcher("gemm", u, i)()
+                launcher("gemm_bf16", u, i)()
         torch.cuda.synchronize()
         gsteps = max(10, args.steps // 4)
         per = {}
         tot_flop = tot_ms = 0.0
         for u in pre_u:
             c = u["case"]
+            # the projection as called: fp16 staging kernel + GEMM, both timed
             ms, _ = timed_region(torch, [launcher("gemm", u, i) for i in range(gsteps)], gsteps)
+            ms_b, _ = timed_region(torch, [launcher("gemm_bf16", u, i) for i in range(gsteps)],
+                                   gsteps)
             flop = 2.0 * c.M * c.N * c.K
             tot_flop += flop
             tot_ms += ms
             per[c.name] = {"M": c.M, "N": c.N, "K": c.K, "us": round(ms * 1e3, 2),
                            "tflops": round(flop / (ms * 1e-3) / 1e12, 1),
-                           "mfma_frac": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4)}
+                           "mfma_frac": round(flop / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+                           "bf16_operands_us": round(ms_b * 1e3, 2)}
         tflops = tot_flop / (tot_ms * 1e-3) / 1e12
         out["prefill_gemm"] = {
             "workload": "prefill chunk M=512: qkv 5120->14336 + gate/up 5120->17408",
             "tflops": round(tflops, 1), "unit": "TFLOP/s",
-            "roofline": {"bound": "mfma", "kernel": "gemm_kernel", "achieved": round(tflops, 1),
+            "note": "us: the projection as the binding calls it (gemm_xprep_kernel staging the "
+                    "activations as fp16, then gemm_kernel on fp16 operands), both kernels "
+                    "inside the timed region; bf16_operands_us: the same projection without a "
+                    "workspace (one gemm_kernel on bf16 operands, the same results bit for bit)",
+            "roofline": {"bound": "mfma", "kernel": "gemm_xprep_kernel + gemm_kernel",
+                         "achieved": round(tflops, 1),
                          "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(tflops / BF16_PEAK_TFLOPS, 4),
                          "traffic": read_traffic("gemm_pre_counters.txt", src_digest("q4p_gemm.hip"),
@@ -493,27 +511,30 @@ def main():
         u = upload(cm, copies_for(algo_bytes(M, 2 * F, K)))
         h = torch.empty((M, F), dtype=torch.int16, device=dev)
 
-        def fused_gemm(i, u=u, h=h):
+        def fused_gemm(i, u=u, h=h, ws=None):
             pc, ps = u["w"][i % len(u["w"])]
-            return lambda: q4.q4proj_gemm_silu_mul(pc, ps, u["g"], u["x"], h, M, F, K)
+            return lambda: q4.q4proj_gemm_silu_mul(pc, ps, u["g"], u["x"], h, M, F, K, workspace=ws)
 
         n = max(10, args.steps // 8)
         for i in range(3):
             fused_gemm(i)()
+            fused_gemm(i, ws=False)()
             launcher("gemm", u, i)()
         ms_f, _ = timed_region(torch, [fused_gemm(i) for i in range(n)], n)
+        ms_fb, _ = timed_region(torch, [fused_gemm(i, ws=False) for i in range(n)], n)
         ms_p, _ = timed_region(torch, [launcher("gemm", u, i) for i in range(n)], n)
         flop = 2.0 * M * 2 * F * K
         fused[f"M={M}"] = {
             "M": M, "F": F, "K": K, "us": round(ms_f * 1e3, 2),
             "tflops": round(flop / (ms_f * 1e-3) / 1e12, 1),
             "mfma_frac": round(flop / (ms_f * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+            "bf16_operands_us": round(ms_fb * 1e3, 2),
             "plain_gemm_2F_us": round(ms_p * 1e3, 2)}
         del u, h
         out["fused_gate_up"] = {
             "workload": "fused gate/up 5120 -> 2x17408 NVFP4 projection + silu(gate)*up -> bf16",
             "kernels": ["gemv_sk_kernel<ROWS, 4, false, true> (M <= 16)",
-                        "gemm_kernel<4, 1, true> (M = 512)"],
+                        "gemm_xprep_kernel + gemm_kernel<4, 1, true> (M = 512)"],
             "per_M": fused,
             "kernel_source_sha256_16": {"gemv": src_digest("q4p_gemv.hip"),
                                         "gemm": src_digest("q4p_gemm.hip")}}

@@ -73,10 +73,13 @@ size_t q4proj_packed_scales_bytes(int64_t N, int64_t K);
 /*
  * Device scratch q4proj_gemv needs for (M, N, K), 1 <= M <= 16 (valid N, K):
  *     8 * (65536 + (KS - 1) * M * N) bytes,
- * where KS (1, 2, 4 or 8) is the number of ranges K is cut into so that one
- * range's activations fit in on-chip memory: KS = 1 while M * ceil(K/128) *
- * 256 <= 128 KiB (e.g. every M = 1 shape up to K = 65536), KS = 2 for M = 7 at
- * K = 17408.  0 otherwise; q4proj_gemm needs none and ignores its workspace.
+ * where KS (1, 2, 4 or 8) is the number of ranges K is cut into.  One
+ * range's activations, M * ceil(K/128) * 256 / KS bytes, must fit in the
+ * 147,392 bytes of on-chip memory a workgroup stages them in; among the
+ * counts that fit, the library picks the one its cost estimate (staging per
+ * workgroup against joins through the workspace) rates fastest: KS = 1 for
+ * every M = 1 shape up to K = 65536, KS = 4 for M = 7 at K = 17408.
+ * 0 otherwise (the GEMM's optional workspace is q4proj_gemm_workspace_bytes).
  * The gemv workspace holds one 64-bit exchange word per output of the row
  * tiles that two workgroups share, and per output and join of the K ranges'
  * partial results.  Ownership and state:
@@ -136,13 +139,38 @@ q4proj_status q4proj_gemv(const uint8_t *packed_codes, const uint8_t *packed_sca
                           void *stream);
 
 /*
+ * Optional device scratch of q4proj_gemm and q4proj_gemm_silu_mul for M rows
+ * of K activations (N does not matter; 0 for invalid arguments):
+ *     roundup256(2 * M * K) + roundup256(4 * M) bytes.
+ * With it the call first stages the activations there as fp16 (each row
+ * scaled by a power of two so that the copy is exact, plus one output
+ * multiplier per row) and runs fp16 matrix-core instructions, which need a
+ * third of the weight-decoding work of the bf16 ones; rows that fp16 cannot
+ * hold exactly (a row spanning more than 29 binades of nonzero magnitudes,
+ * or a global scale whose row multiplier would leave the normal range) keep
+ * bf16 for their 128-row block.  Every product is exact either way and the
+ * sums run in the same order, so the results equal those without a
+ * workspace bit for bit (barring fp32 overflow or underflow of the unscaled
+ * sums).  Ownership: the caller's, 16-byte aligned, overlapping no other
+ * argument; no contents are required on entry and the call leaves its
+ * scratch there, so it must not share memory with a gemv, silu or argmax
+ * workspace (those must stay zero-filled).  Calls that may overlap in time
+ * (different streams) need separate workspaces.
+ */
+size_t q4proj_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K);
+
+/*
  * q4proj_gemm — prefill-chunk projection, any M >= 1 (sized for M = 512).
  * Same arguments and result definition as q4proj_gemv.  Dequantises weight
- * tiles to bf16 (exactly: q*s has at most 6 significant bits) and runs bf16
- * matrix-core instructions with fp32 accumulation; g is applied once per
- * output after accumulation.  Deterministic.
- * workspace is not used (may be NULL with workspace_bytes 0).
- * Errors: EINVAL, EDEVICE, EHIP.
+ * tiles exactly (q*s has at most 6 significant bits) and runs matrix-core
+ * instructions with fp32 accumulation; g is applied once per output after
+ * accumulation.  Deterministic.
+ * workspace: NULL (workspace_bytes ignored): bf16 operands; or at least
+ * q4proj_gemm_workspace_bytes(M, N, K) bytes as described there: fp16
+ * operands, the same results, faster.
+ * Errors: EINVAL (as q4proj_gemv; also a misaligned or overlapping
+ *         workspace), EWORKSPACE (a workspace smaller than required),
+ *         EDEVICE, EHIP.
  */
 q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
                           float global_scale, const uint16_t *x, float *y, int64_t M,
@@ -247,10 +275,13 @@ q4proj_status q4proj_pack_gate_up(const uint8_t *gate_codes, const uint8_t *gate
  * q4proj_gemv_silu_mul for any M >= 1 (sized for the M = 512 prefill chunk):
  * the bf16 matrix-core projection of q4proj_gemm over the fused [2F][K]
  * weight, h[M][F] = bf16(silu(g*gate) * (g*up)) written in place of y.
- * Same layouts and result definition as q4proj_gemv_silu_mul; workspace is
- * not used (may be NULL with workspace_bytes 0).  Deterministic.
+ * Same layouts and result definition as q4proj_gemv_silu_mul.  workspace:
+ * as q4proj_gemm's, q4proj_gemm_workspace_bytes(M, 2F, K) bytes or NULL.
+ * Deterministic.
  * Errors: EINVAL (null pointer, M/F/K <= 0, F % 8 != 0, K % 16 != 0,
- *         misaligned x or h, h overlapping an input), EDEVICE, EHIP.
+ *         misaligned x, h or workspace, h or workspace overlapping an
+ *         input), EWORKSPACE (a workspace smaller than required), EDEVICE,
+ *         EHIP.
  */
 q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
                                    float global_scale, const uint16_t *x, uint16_t *h,

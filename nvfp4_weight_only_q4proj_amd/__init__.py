@@ -50,6 +50,8 @@ _lib.q4proj_gemv.argtypes = _PROJ_ARGS
 _lib.q4proj_gemv.restype = ctypes.c_int
 _lib.q4proj_gemm.argtypes = _PROJ_ARGS
 _lib.q4proj_gemm.restype = ctypes.c_int
+_lib.q4proj_gemm_workspace_bytes.argtypes = [_i64, _i64, _i64]
+_lib.q4proj_gemm_workspace_bytes.restype = _sz
 _lib.q4proj_gemv_noalloc.argtypes = [_vp, _vp, _f32, _vp, _vp, _i64, _i64, _i64, _vp]
 _lib.q4proj_gemv_noalloc.restype = ctypes.c_int
 _lib.q4proj_silu_mul_workspace_bytes.argtypes = [_i64, _i64, _i64]
@@ -75,7 +77,7 @@ _lib.q4proj_last_hip_error.restype = ctypes.c_char_p
 #: Exported symbols declared by include/q4proj.h.
 SYMBOLS = ("q4proj_packed_codes_bytes", "q4proj_packed_scales_bytes", "q4proj_workspace_bytes",
            "q4proj_pack", "q4proj_pack_gate_up", "q4proj_unpack", "q4proj_gemv", "q4proj_gemm",
-           "q4proj_gemv_noalloc",
+           "q4proj_gemm_workspace_bytes", "q4proj_gemv_noalloc",
            "q4proj_silu_mul_workspace_bytes", "q4proj_gemv_silu_mul", "q4proj_gemm_silu_mul",
            "q4proj_argmax_workspace_bytes", "q4proj_gemv_argmax",
            "q4proj_quantize_workspace_bytes", "q4proj_quantize",
@@ -122,6 +124,11 @@ def q4proj_workspace_bytes(M: int, N: int, K: int) -> int:
 @functools.lru_cache(maxsize=4096)
 def q4proj_silu_mul_workspace_bytes(M: int, F: int, K: int) -> int:
     return int(_lib.q4proj_silu_mul_workspace_bytes(M, F, K))
+
+
+@functools.lru_cache(maxsize=4096)
+def q4proj_gemm_workspace_bytes(M: int, N: int, K: int) -> int:
+    return int(_lib.q4proj_gemm_workspace_bytes(M, N, K))
 
 
 # The checks below sit on the decode path (one call per projection, ~12 us of
@@ -221,6 +228,7 @@ def q4proj_unpack(packed_codes: torch.Tensor, packed_scales: torch.Tensor, N: in
 
 
 _workspaces: dict = {}
+_gemm_scratch: dict = {}
 
 
 def _stream_handle_and_obj(dev: int, stream):
@@ -263,6 +271,36 @@ def default_workspace(device, nbytes: int, stream=None):
     return ws
 
 
+def gemm_scratch(device, nbytes: int, stream=None):
+    """A device buffer of at least nbytes for q4proj_gemm / q4proj_gemm_silu_mul
+    calls on `stream` (default: the device's current stream) that pass no
+    workspace: the GEMMs stage their fp16 activations there.  Its contents
+    do not matter (it is never zero-filled) and it is kept apart from the
+    zero-filled default workspaces of the GEMV entry points.  One per
+    (device, stream), allocated on that stream."""
+    dev = device if isinstance(device, int) else (
+        torch.device(device).index if torch.device(device).index is not None
+        else torch.cuda.current_device())
+    key = (dev, _stream(dev, stream))
+    ws = _gemm_scratch.get(key)
+    if ws is None or ws.numel() < nbytes:
+        _, sobj = _stream_handle_and_obj(dev, stream)
+        with torch.cuda.stream(sobj):
+            ws = torch.empty(nbytes, dtype=torch.uint8, device=torch.device("cuda", dev))
+        _gemm_scratch[key] = ws
+    return ws
+
+
+def _gemm_workspace(dev, workspace, M, N, K, stream):
+    """The workspace a GEMM call passes: workspace=None takes the per-stream
+    scratch (fp16 operands), workspace=False none (bf16 operands)."""
+    if workspace is None:
+        return gemm_scratch(dev, q4proj_gemm_workspace_bytes(M, N, K), stream)
+    if workspace is False:
+        return None
+    return workspace
+
+
 def _bf16_bits(t, name):
     """A bfloat16 tensor as its 16-bit patterns (a view); int16/uint16 pass."""
     if isinstance(t, torch.Tensor) and t.dtype == torch.bfloat16:
@@ -283,7 +321,9 @@ def _proj_args(name, packed_codes, packed_scales, global_scale, x, y, M, N, K, w
     _need(x, "x", x.dtype, M * K, dev)
     _need(y, "y", torch.float32, M * N, dev)
     ws_ptr, ws_bytes = None, 0
-    if workspace is None and name == "q4proj_gemv":
+    if name == "q4proj_gemm":
+        workspace = _gemm_workspace(dev, workspace, M, N, K, stream)
+    elif workspace is None and name == "q4proj_gemv":
         workspace = default_workspace(dev, q4proj_workspace_bytes(M, N, K), stream)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)
@@ -325,7 +365,10 @@ def q4proj_gemv_noalloc(packed_codes, packed_scales, global_scale: float, x, y, 
 
 def q4proj_gemm(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,
                 workspace=None, stream=None) -> None:
-    """y[M][N] fp32 = x[M][K] bf16 . dequant(W)^T for any M >= 1."""
+    """y[M][N] fp32 = x[M][K] bf16 . dequant(W)^T for any M >= 1.
+    workspace: None takes the stream's GEMM scratch (fp16 operands), False
+    runs without one (bf16 operands, the same results), or a uint8 tensor of
+    q4proj_gemm_workspace_bytes(M, N, K) bytes."""
     _proj(_lib.q4proj_gemm, "q4proj_gemm", packed_codes, packed_scales, global_scale, x, y, M, N,
           K, workspace, stream)
 
@@ -340,7 +383,8 @@ def q4proj_gemv_silu_mul(packed_codes, packed_scales, global_scale: float, x, h,
 
 def q4proj_gemm_silu_mul(packed_codes, packed_scales, global_scale: float, x, h, M: int, F: int,
                          K: int, workspace=None, stream=None) -> None:
-    """As q4proj_gemv_silu_mul for any M >= 1 (matrix-core path, no workspace)."""
+    """As q4proj_gemv_silu_mul for any M >= 1 (matrix-core path); workspace as
+    q4proj_gemm's (N = 2F)."""
     _silu_mul(_lib.q4proj_gemm_silu_mul, "q4proj_gemm_silu_mul", packed_codes, packed_scales,
               global_scale, x, h, M, F, K, workspace, stream)
 
@@ -356,7 +400,9 @@ def _silu_mul_args(name, packed_codes, packed_scales, global_scale, x, h, M, F, 
     _need(x, "x", x.dtype, M * K, dev)
     _need(h, "h", h.dtype, M * F, dev)
     ws_ptr, ws_bytes = None, 0
-    if workspace is None and name == "q4proj_gemv_silu_mul":
+    if name == "q4proj_gemm_silu_mul":
+        workspace = _gemm_workspace(dev, workspace, M, N, K, stream)
+    elif workspace is None and name == "q4proj_gemv_silu_mul":
         workspace = default_workspace(dev, q4proj_silu_mul_workspace_bytes(M, F, K), stream)
     if workspace is not None:
         _need(workspace, "workspace", torch.uint8, workspace.numel(), dev)

@@ -10,6 +10,7 @@
 
 #include <atomic>
 #include <cstring>
+#include <initializer_list>
 
 #include "q4p_launch.h"
 #include "q4p_layout.h"
@@ -105,6 +106,31 @@ q4proj_status check_silu_mul(const uint8_t *pc, const uint8_t *ps, const uint16_
     if (overlap(h, hbytes, x, xbytes) || overlap(h, hbytes, pc, q4proj_packed_codes_bytes(2 * F, K)) ||
         overlap(h, hbytes, ps, q4proj_packed_scales_bytes(2 * F, K)))
         return Q4P_EINVAL;
+    return Q4P_OK;
+}
+
+struct Span {
+    const void *p;
+    size_t n;
+};
+
+// The optional GEMM workspace: none (NULL) is fine; one that is given must
+// be 16-byte aligned, hold q4proj_gemm_workspace_bytes(M, N, K) bytes and
+// overlap no other argument.
+q4proj_status check_gemm_workspace(const void *ws, size_t ws_bytes, int64_t M, int64_t N,
+                                   int64_t K, std::initializer_list<Span> args)
+{
+    if (!ws)
+        return Q4P_OK;
+    const size_t need = q4p::gemm_workspace_bytes(M, K);
+    (void)N;
+    if (ws_bytes < need)
+        return Q4P_EWORKSPACE;
+    if (!aligned(ws, 16))
+        return Q4P_EINVAL;
+    for (const Span &a : args)
+        if (overlap(ws, need, a.p, a.n))
+            return Q4P_EINVAL;
     return Q4P_OK;
 }
 
@@ -299,16 +325,22 @@ q4proj_status q4proj_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *p
                                    int64_t F, int64_t K, void *workspace, size_t workspace_bytes,
                                    void *stream)
 {
-    (void)workspace;
-    (void)workspace_bytes;
     q4proj_status st = check_silu_mul(packed_codes, packed_scales, x, h, M, F, K);
+    if (st != Q4P_OK)
+        return st;
+    const int64_t N = 2 * F;
+    st = check_gemm_workspace(workspace, workspace_bytes, M, N, K,
+                              {{x, (size_t)M * (size_t)K * 2}, {h, (size_t)M * (size_t)F * 2},
+                               {packed_codes, q4proj_packed_codes_bytes(N, K)},
+                               {packed_scales, q4proj_packed_scales_bytes(N, K)}});
     if (st != Q4P_OK)
         return st;
     st = check_device();
     if (st != Q4P_OK)
         return st;
     return record_hip(q4p::launch_gemm_silu_mul(packed_codes, packed_scales, global_scale, x, h,
-                                                M, F, K, static_cast<hipStream_t>(stream)));
+                                                M, F, K, workspace,
+                                                static_cast<hipStream_t>(stream)));
 }
 
 size_t q4proj_argmax_workspace_bytes(int64_t M, int64_t N, int64_t K)
@@ -405,20 +437,33 @@ q4proj_status q4proj_quantize(const uint16_t *w, int64_t N, int64_t K, uint8_t *
                                            static_cast<hipStream_t>(stream)));
 }
 
+size_t q4proj_gemm_workspace_bytes(int64_t M, int64_t N, int64_t K)
+{
+    if (M <= 0 || M > (int64_t)1 << 24 || !shape_ok(N, K))
+        return 0;
+    return q4p::gemm_workspace_bytes(M, K);
+}
+
 q4proj_status q4proj_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales,
                           float global_scale, const uint16_t *x, float *y, int64_t M, int64_t N,
                           int64_t K, void *workspace, size_t workspace_bytes, void *stream)
 {
-    (void)workspace;
     q4proj_status st = check_projection(packed_codes, packed_scales, x, y, M, N, K,
                                         workspace_bytes, 0);
+    if (st != Q4P_OK)
+        return st;
+    st = check_gemm_workspace(workspace, workspace_bytes, M, N, K,
+                              {{x, (size_t)M * (size_t)K * 2},
+                               {y, (size_t)M * (size_t)N * sizeof(float)},
+                               {packed_codes, q4proj_packed_codes_bytes(N, K)},
+                               {packed_scales, q4proj_packed_scales_bytes(N, K)}});
     if (st != Q4P_OK)
         return st;
     st = check_device();
     if (st != Q4P_OK)
         return st;
     return record_hip(q4p::launch_gemm(packed_codes, packed_scales, global_scale, x, y, M, N, K,
-                                       static_cast<hipStream_t>(stream)));
+                                       workspace, static_cast<hipStream_t>(stream)));
 }
 
 const char *q4proj_status_string(q4proj_status s)

@@ -50,11 +50,23 @@
 //  * Dequantisation to bf16 with the e4m3 scale folded in is exact: q*s has
 //    at most 6 significant bits.  fp32 accumulation in the MFMA; y = g * acc
 //    stored once.
+//  * fp16 operands when the caller gives a workspace: a staging kernel first
+//    copies every activation row to fp16 scaled by a power of two chosen so
+//    that the copy is exact, with g times the inverse power as the row's
+//    output multiplier.  The weights then dequantise to fp16 with one packed
+//    multiply per pair (4 conversions + 4 multiplies per 8 codes instead of
+//    4 + 8 + 4 for bf16, which has no packed arithmetic on gfx950), and the
+//    fp16 MFMAs sum the same exact products in the same order, so y is the
+//    same bit for bit.  A block holding a row that fp16 cannot carry exactly
+//    runs the bf16 loop; the choice is made once per workgroup from the row
+//    multipliers, before the activation loads go out.
 //  * SILU variant (fused gate/up weight, 8 gate rows and the matching 8 up
 //    rows per 16-row tile): the lanes r and r + 8 that hold a gate/up pair
 //    swap values by a row rotate and write h = bf16(silu(g*gate) * (g*up))
 //    instead of y; lanes r < 8 take rows 4gq, 4gq+1 of each block and lanes
 //    r >= 8 rows 4gq+2, 4gq+3, so every lane evaluates two epilogues.
+#include <type_traits>
+
 #include "q4p_device.h"
 #include "q4p_launch.h"
 
@@ -104,6 +116,29 @@ __device__ __forceinline__ bf16x8_t dequant8(uint32_t wd, float s)
     return __builtin_bit_cast(bf16x8_t, v);
 }
 
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+
+// The same eight products as fp16: each e2m1 pair converts exactly to fp16
+// and one packed fp16 multiply applies the scale, exactly (q*s has at most 6
+// significant bits and lies in [2^-10, 2688], inside fp16's normal range).
+__device__ __forceinline__ f16x8_t dequant8h(uint32_t wd, _Float16 s)
+{
+    const f16x2_t s2 = {s, s};
+    const f16x2_t v0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 0) * s2;
+    const f16x2_t v1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 1) * s2;
+    const f16x2_t v2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 2) * s2;
+    const f16x2_t v3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(wd, 1.0f, 3) * s2;
+    return (f16x8_t){v0[0], v0[1], v1[0], v1[1], v2[0], v2[1], v3[0], v3[1]};
+}
+
+// OCP e4m3 byte SEL of w -> fp16 (exact: every e4m3 value is an fp16 value)
+template <int SEL>
+__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t w)
+{
+    return __builtin_amdgcn_cvt_scalef32_f16_fp8((f16x2_t){0, 0}, (int)w, 1.0f, SEL, false)[0];
+}
+
 // Position of code slot s (16 bytes) of a packed tile in a weight stage.
 // A k-step's read takes 8 bytes of slots 32h + r and 32h + r + 16 (r < 16,
 // h = 0, 1) in one ds_read2_b64, so without a swizzle the slots r, r + 8,
@@ -124,7 +159,8 @@ constexpr int kWaitLgkm0 = 0xc07f;
 template <int Q, int RT, bool SILU>
 __global__ void __launch_bounds__(512)
 gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ pscales, float g,
-            const uint16_t *__restrict__ x, void *__restrict__ out, int M, int N, int64_t ldy,
+            const uint16_t *__restrict__ x, const uint16_t *__restrict__ xh,
+            const float *__restrict__ rowmul, void *__restrict__ out, int M, int N, int64_t ldy,
             int K, int KT, int NT, int buf_out)
 {
     constexpr int TT = 4 * Q + RT;                         // tiles per workgroup (== T)
@@ -141,6 +177,8 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     __shared__ __attribute__((aligned(16))) uint8_t sw0[kWStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t sw1[kWStageBytes];
     __shared__ __attribute__((aligned(16))) uint8_t sw2[kWStageBytes];
+    // per-row output multipliers of the fp16 run (rowmul of the block's rows)
+    __shared__ __attribute__((aligned(16))) float srow[kBM];
 
     const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
     const int w = wave & 3;                                // tile group
@@ -201,11 +239,11 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
     // that is not live (past the last k-tile) gets a buffer of size 0 and
     // only writes zeros into a free stage.
     constexpr int kLoads = 4 + kWLoadsPerWave;
-    auto issue_load = [&](int n, int c, bool live, uint8_t *sx, uint8_t *sw) __attribute__((always_inline)) {
+    auto issue_load = [&](int n, int c, bool live, uint8_t *sx, uint8_t *sw, const uint16_t *xa) __attribute__((always_inline)) {
         if (n < 4) {
             const int i = n < 4 ? n : 0;
             const bool last = ragged && c == KT - 1;
-            load_lds16(make_rsrc(x, live ? xbytes : 0u), sx + 1024 * (4 * wave + n),
+            load_lds16(make_rsrc(xa, live ? xbytes : 0u), sx + 1024 * (4 * wave + n),
                        last ? xlast[i] : xoff[i], last ? 0u : 256u * (uint32_t)c);
         } else {
             const int q = n - 4 < kWLoadsPerWave ? n - 4 : 0;
@@ -220,27 +258,17 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
             load_lds16(make_rsrc(base, bytes), sw + wlds[q], woff[q], adv);
         }
     };
-    auto issue_stage = [&](int c, bool live, uint8_t *sx, uint8_t *sw) __attribute__((always_inline)) {
+    // the weight loads (n >= 4) and the activation loads (n < 4) of a stage
+    auto issue_wstage = [&](int c, bool live, uint8_t *sw) __attribute__((always_inline)) {
 #pragma unroll
-        for (int n = 0; n < kLoads; ++n)
-            issue_load(n, c, live, sx, sw);
+        for (int n = 4; n < kLoads; ++n)
+            issue_load(n, c, live, nullptr, sw, nullptr);
     };
-
-    // ---- accumulators -------------------------------------------------------
-    // accF[j][i]: whole tile w*Q + j, row block i ^ rb.
-    // accR[j][i]: remaining tile, row block rb + i.
-    floatx4_t accF[Q > 0 ? Q : 1][8];
-    floatx4_t accR[RB > 0 ? RB : 1][RR];
+    auto issue_xstage = [&](int c, bool live, uint8_t *sx, const uint16_t *xa) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < Q; ++j)
-#pragma unroll
-        for (int i = 0; i < 8; ++i)
-            accF[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int j = 0; j < RB; ++j)
-#pragma unroll
-        for (int i = 0; i < RR; ++i)
-            accR[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < 4; ++n)
+            issue_load(n, c, live, sx, nullptr, xa);
+    };
 
     // code slots (r, 2h) and (r, 2h+1) hold this lane's k-values; the byte
     // permute picks block 2d + gq/2 of each
@@ -265,21 +293,14 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
                 rbase[k] = ab + (((2 * k) ^ rb) << 12);
         }
     };
-    auto row_operand = [&](const uint8_t *const *rbase, int i) __attribute__((always_inline)) {
-        const uint8_t *pa = RT == 0 ? rbase[0] + (i << 12)
-                          : RT == 2 ? rbase[i >> 2] + ((i & 3) << 12)
-                                    : rbase[i >> 1] + ((i & 1) << 12);
-        return *reinterpret_cast<const bf16x8_t *>(pa);
-    };
 
     // ---- software-pipelined k-loop --------------------------------------------
     // NB operands per k-step: the Q whole tiles, then the wave's remaining
     // tiles.  Raw code words and scales of one k-tile for this wave (pW, qW,
-    // sW) and the dequantised operands of its two k-steps (b0, b1).
+    // sW).
     constexpr int NB = Q + RB;
     uint2 pW[NB], qW[NB];
     uint32_t sW[NB];
-    bf16x8_t b0[NB], b1[NB];
 
     // this wave's code bytes (blocks 4kh..4kh+3 of two slots) and scales of
     // tile j of one landed stage; the scale of block 4kh + 2dd + gq/2 moved
@@ -292,247 +313,433 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
         sW[j] = *reinterpret_cast<const uint32_t *>(
                     sw + TT * kTileCodeBytes + jt * kTileScaleBytes + scale_lane) >> (8 * (gq >> 1));
     };
-    // operand of tile j for the wave's k-step dd from the raw words
-    auto dequant_tile = [&](int j, int dd) __attribute__((always_inline)) {
-        const uint32_t wd = __builtin_amdgcn_perm(dd ? qW[j].y : qW[j].x, dd ? pW[j].y : pW[j].x, sel);
-        return dequant8(wd, dd ? e4m3_to_f32<2>(sW[j]) : e4m3_to_f32<0>(sW[j]));
-    };
-    // the MFMAs of the wave's k-step dd on the activations of stage sx with
-    // operands b; fill(i) is independent work placed after row block i
-    auto mfma_step = [&](int dd, const uint8_t *sx, const bf16x8_t *b, auto fill) __attribute__((always_inline)) {
-        const int d = 2 * kh + dd;
-        const uint8_t *rbase[4];
-        row_bases(sx + a_lane + (((4 * d + gq) ^ r) << 4), rbase);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const bf16x8_t a = row_operand(rbase, i);
-#pragma unroll
-            for (int j = 0; j < Q; ++j)
-                accF[j][i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b[j], accF[j][i], 0, 0, 0);
-            if (i < RR) {
-#pragma unroll
-                for (int j = 0; j < RB; ++j)
-                    accR[j][i < RR ? i : 0] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                        a, b[Q + j], accR[j][i < RR ? i : 0], 0, 0, 0);
-            }
-            fill(i);
-        }
-    };
 
-    // One k-tile c.  Phase 1: the MFMAs of the first k-step, with the second
-    // step's operands dequantised in between.  Then a barrier: stage c+1 has
-    // landed everywhere and every wave is done with stage c-1.  Phase 2: the
-    // MFMAs of the second k-step, with the stage loads of k-tile c+2 (into the
-    // stage of c-1) and the reading and dequantising of k-tile c+1's first
-    // step in between.  So no wave ever waits for its own dequantisation, and
-    // each stage has about one k-tile to land.
-    auto ktile = [&](int c, const uint8_t *sxc, const uint8_t *swn, uint8_t *sxl, uint8_t *swl) __attribute__((always_inline)) {
-        mfma_step(0, sxc, b0, [&](int i) __attribute__((always_inline)) {
-            if (i < NB)
-                b1[i < NB ? i : 0] = dequant_tile(i < NB ? i : 0, 1);
-        });
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                 // lgkmcnt(0)
-        __builtin_amdgcn_s_barrier();
-        const bool live = c + 2 < KT;
-        mfma_step(1, sxc, b1, [&](int i) __attribute__((always_inline)) {
-            if (i < kLoads)
-                issue_load(i, c + 2, live, sxl, swl);
-            // tile i's words are read two row blocks before they are used
-            if (i < NB)
-                read_tile(swn, i < NB ? i : 0);
-            if (i >= 2 && i - 2 < NB)
-                b0[i >= 2 && i - 2 < NB ? i - 2 : 0] = dequant_tile(i >= 2 && i - 2 < NB ? i - 2 : 0, 0);
-        });
-        static_assert(NB <= 6, "every tile is dequantised inside the row loop");
-    };
-
-    // stages 0 and 1 (skipped past the last k-tile) land before the loop;
-    // afterwards every k-tile issues the loads of the k-tile two ahead
-    issue_stage(0, true, sx0, sw0);
-    issue_stage(1, KT > 1, sx1, sw1);
-    // stage 1's loads (the last kLoads issued) may still be in flight; the
-    // first k-tile's barrier waits for them
-    static_assert(kLoads < 16, "vmcnt immediate");
-    __builtin_amdgcn_s_waitcnt(0x0f70 | kLoads);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-#pragma unroll
-    for (int j = 0; j < NB; ++j) {
-        read_tile(sw0, j);
-        b0[j] = dequant_tile(j, 0);
-    }
-    for (int c = 0; c < KT; c += 3) {
-        ktile(c, sx0, sw1, sx2, sw2);
-        if (c + 1 < KT)
-            ktile(c + 1, sx1, sw2, sx0, sw0);
-        if (c + 2 < KT)
-            ktile(c + 2, sx2, sw0, sx1, sw1);
-    }
-
-
-    // ---- add the k-halves ------------------------------------------------------
-    // Wave kh finishes row-block positions 4kh..4kh+3 of its whole tiles and
-    // the kh-th half of its remaining-tile blocks.  Both waves of a pair hand
-    // the partner the half it finishes, all through LDS at once: fragment f
-    // (64 lanes x 16 bytes) of wave v sits in its own slot of the now free
-    // stage buffers, so one barrier separates the writes from the reads, and
-    // both waves of a SIMD then share the epilogue.
-    constexpr int HR = RR / 2;                                 // remaining blocks kept per wave
-    constexpr int kKeep = 4 * Q + RB * HR;                     // fragments kept (and handed over)
-    static_assert(kKeep <= 8 || 2 * (kKeep - 8 < 8 ? kKeep - 8 : 8) * 1024 <= kWStageBytes,
-                  "fragments 8..15 of waves 4..7: two waves per weight stage");
-    static_assert(kKeep <= 16 || (kKeep <= 18 && 8 * 2048 <= kWStageBytes),
-                  "fragments 16, 17: the third weight stage");
-    static_assert(3 * (kXStageBytes + kWStageBytes) <= 160 * 1024, "LDS of one CU");
-    floatx4_t keep[kKeep > 0 ? kKeep : 1];
-    {
-        // every wave is past its last LDS read of the stages (the last
-        // compute ended with them) and its trailing zero-writing loads have
-        // landed, so the stage buffers are free
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
-        auto slot = [&](int v, int f) __attribute__((always_inline)) {
-            uint8_t *base;
-            if (f < 8)
-                base = (v < 4 ? sx0 : sx1) + (v & 3) * 8192 + f * 1024;
-            else if (f < 16)
-                base = v < 4 ? sx2 + v * 8192 + (f - 8) * 1024
-                             : (v < 6 ? sw0 : sw1) + (v & 1) * (kKeep - 8 < 8 ? kKeep - 8 : 8) * 1024 + (f - 8) * 1024;
-            else
-                base = sw2 + v * 2048 + (f - 16) * 1024;
-            return reinterpret_cast<floatx4_t *>(base) + lane;
-        };
-        const bool upper = kh != 0;
+    // The k-loop and epilogue on one operand type.  F16: fp16 activations xa
+    // (each row scaled by a power of two, see gemm_xprep_kernel) times fp16
+    // weights; otherwise the bf16 activations xa times bf16 weights.  The
+    // products are exact either way and the MFMAs accumulate them in the same
+    // order.  The weight loads of stages 0 and 1 are already in flight.
+    auto run = [&](auto f16_tag, const uint16_t *xa) __attribute__((always_inline)) {
+        constexpr bool F16 = decltype(f16_tag)::value;
+        using op_t = typename std::conditional<F16, f16x8_t, bf16x8_t>::type;
+        // ---- accumulators -------------------------------------------------------
+        // accF[j][i]: whole tile w*Q + j, row block i ^ rb.
+        // accR[j][i]: remaining tile, row block rb + i.
+        floatx4_t accF[Q > 0 ? Q : 1][8];
+        floatx4_t accR[RB > 0 ? RB : 1][RR];
 #pragma unroll
         for (int j = 0; j < Q; ++j)
 #pragma unroll
-            for (int ii = 0; ii < 4; ++ii) {
-                const floatx4_t lo = accF[j][ii], hi = accF[j][ii + 4];
-                *slot(wave, 4 * j + ii) = upper ? lo : hi;
-                keep[4 * j + ii] = upper ? hi : lo;
-            }
+            for (int i = 0; i < 8; ++i)
+                accF[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int j = 0; j < RB; ++j)
 #pragma unroll
-            for (int ii = 0; ii < HR; ++ii) {
-                const floatx4_t lo = accR[j][ii], hi = accR[j][ii + HR];
-                *slot(wave, 4 * Q + HR * j + ii) = upper ? lo : hi;
-                keep[4 * Q + HR * j + ii] = upper ? hi : lo;
+            for (int i = 0; i < RR; ++i)
+                accR[j][i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+        // the dequantised operands of the wave's two k-steps
+        op_t b0[NB], b1[NB];
+        auto row_operand = [&](const uint8_t *const *rbase, int i) __attribute__((always_inline)) {
+            const uint8_t *pa = RT == 0 ? rbase[0] + (i << 12)
+                              : RT == 2 ? rbase[i >> 2] + ((i & 3) << 12)
+                                        : rbase[i >> 1] + ((i & 1) << 12);
+            return *reinterpret_cast<const op_t *>(pa);
+        };
+        // operand of tile j for the wave's k-step dd from the raw words
+        auto dequant_tile = [&](int j, int dd) __attribute__((always_inline)) {
+            const uint32_t wd = __builtin_amdgcn_perm(dd ? qW[j].y : qW[j].x, dd ? pW[j].y : pW[j].x, sel);
+            if constexpr (F16)
+                return dequant8h(wd, dd ? e4m3_to_f16<2>(sW[j]) : e4m3_to_f16<0>(sW[j]));
+            else
+                return dequant8(wd, dd ? e4m3_to_f32<2>(sW[j]) : e4m3_to_f32<0>(sW[j]));
+        };
+        auto mma = [&](op_t a, op_t bb, floatx4_t acc) __attribute__((always_inline)) {
+            if constexpr (F16)
+                return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, bb, acc, 0, 0, 0);
+            else
+                return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, bb, acc, 0, 0, 0);
+        };
+        // the MFMAs of the wave's k-step dd on the activations of stage sx with
+        // operands b; fill(i) is independent work placed after row block i
+        auto mfma_step = [&](int dd, const uint8_t *sx, const op_t *b, auto fill) __attribute__((always_inline)) {
+            const int d = 2 * kh + dd;
+            const uint8_t *rbase[4];
+            row_bases(sx + a_lane + (((4 * d + gq) ^ r) << 4), rbase);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const op_t a = row_operand(rbase, i);
+#pragma unroll
+                for (int j = 0; j < Q; ++j)
+                    accF[j][i] = mma(a, b[j], accF[j][i]);
+                if (i < RR) {
+#pragma unroll
+                    for (int j = 0; j < RB; ++j)
+                        accR[j][i < RR ? i : 0] = mma(a, b[Q + j], accR[j][i < RR ? i : 0]);
+                }
+                fill(i);
             }
+        };
+
+        // One k-tile c.  Phase 1: the MFMAs of the first k-step, with the second
+        // step's operands dequantised in between.  Then a barrier: stage c+1 has
+        // landed everywhere and every wave is done with stage c-1.  Phase 2: the
+        // MFMAs of the second k-step, with the stage loads of k-tile c+2 (into the
+        // stage of c-1) and the reading and dequantising of k-tile c+1's first
+        // step in between.  So no wave ever waits for its own dequantisation, and
+        // each stage has about one k-tile to land.
+        auto ktile = [&](int c, const uint8_t *sxc, const uint8_t *swn, uint8_t *sxl, uint8_t *swl) __attribute__((always_inline)) {
+            mfma_step(0, sxc, b0, [&](int i) __attribute__((always_inline)) {
+                if (i < NB)
+                    b1[i < NB ? i : 0] = dequant_tile(i < NB ? i : 0, 1);
+            });
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);                 // lgkmcnt(0)
+            __builtin_amdgcn_s_barrier();
+            const bool live = c + 2 < KT;
+            mfma_step(1, sxc, b1, [&](int i) __attribute__((always_inline)) {
+                if (i < kLoads)
+                    issue_load(i, c + 2, live, sxl, swl, xa);
+                // tile i's words are read two row blocks before they are used
+                if (i < NB)
+                    read_tile(swn, i < NB ? i : 0);
+                if (i >= 2 && i - 2 < NB)
+                    b0[i >= 2 && i - 2 < NB ? i - 2 : 0] = dequant_tile(i >= 2 && i - 2 < NB ? i - 2 : 0, 0);
+            });
+            static_assert(NB <= 6, "every tile is dequantised inside the row loop");
+        };
+
+        // the activations of stages 0 and 1 (skipped past the last k-tile);
+        // afterwards every k-tile issues the loads of the k-tile two ahead.
+        // Stage 1's activation loads (the last 4 issued) may still be in
+        // flight; the first k-tile's barrier waits for them.
+        issue_xstage(0, true, sx0, xa);
+        issue_xstage(1, KT > 1, sx1, xa);
+        __builtin_amdgcn_s_waitcnt(0x0f70 | 4);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
 #pragma unroll
-        for (int f = 0; f < kKeep; ++f)
-            keep[f] += *slot(wave ^ 4, f);
-    }
-    // fragment f of keep: tile and 16-row block (wave-uniform)
-    auto frag_tile = [&](int f) __attribute__((always_inline)) {
-        return f < 4 * Q ? tile0 + w * Q + f / 4
-                         : tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + (f - 4 * Q) / (HR > 0 ? HR : 1));
-    };
-    auto frag_block = [&](int f) __attribute__((always_inline)) {
-        return f < 4 * Q ? (4 * kh + f % 4) ^ rb : rb + HR * kh + (f - 4 * Q) % (HR > 0 ? HR : 1);
-    };
-
-    // ---- epilogue: lane (r, gq) holds rows 4*gq + i of each 16-row block ----
-    if (SILU) {
-        const bool hi = r >= 8;
-        if (buf_out) {
-            // bf16 h through buffer stores as y below (2 bytes per output, rows
-            // past M dropped at the buffer's end)
-            const uint32_t hstride = (uint32_t)ldy * 2u;        // bytes per row of h
-            const __amdgpu_buffer_rsrc_t hrs = make_rsrc(out, (uint32_t)M * hstride);
-            // lanes r < 8 write rows 4gq, 4gq+1 of a block, lanes r >= 8 rows
-            // 4gq+2, 4gq+3; output f = 8t + r%8
-            const uint32_t lane_row = (uint32_t)(4 * gq + (hi ? 2 : 0)) * hstride;
-#pragma unroll
-            for (int f = 0; f < kKeep; ++f) {
-                const int t = frag_tile(f);
-                if (t < NT) {
-                    const floatx4_t v = keep[f];
-                    const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-                    const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
-                    const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
-                    const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
-                    const uint32_t fo = 8u * (uint32_t)t + (uint32_t)(r & 7);
-                    const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(
-                        (int)((uint32_t)(m0 + 16 * frag_block(f)) * hstride));
-                    const uint32_t off = lane_row + fo * 2u + row;
-                    __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * ga, g * ua), hrs, (int)off, 0, 0);
-                    __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(g * gb, g * ub), hrs,
-                                                          (int)(off + hstride), 0, 0);
-                }
-            }
-        } else {
-            // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
-            uint16_t *h = static_cast<uint16_t *>(out);
-#pragma unroll
-            for (int f = 0; f < kKeep; ++f) {
-                const int t = frag_tile(f);
-                if (t < NT) {
-                    const floatx4_t v = keep[f];
-                    const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
-                    const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
-                    const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
-                    const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
-                    const int m = m0 + 16 * frag_block(f) + 4 * gq + (hi ? 2 : 0);
-                    const int64_t fo = 8 * (int64_t)t + (r & 7);
-                    if (m < M)
-                        h[(int64_t)m * ldy + fo] = silu_mul_bf16(g * ga, g * ua);
-                    if (m + 1 < M)
-                        h[(int64_t)(m + 1) * ldy + fo] = silu_mul_bf16(g * gb, g * ub);
-                }
-            }
+        for (int j = 0; j < NB; ++j) {
+            read_tile(sw0, j);
+            b0[j] = dequant_tile(j, 0);
         }
-        return;
-    }
-    if (buf_out) {
-        // y through buffer stores: the row part of each offset is wave-uniform
-        // and the lane part fixed, so a store costs one add.  Rows past M lie
-        // past the end of the buffer (buf_out: the launch's rows plus one block
-        // stay under 2 GiB of y) and are dropped by the hardware instead of
-        // being tested per store.
-        const uint32_t rstride = (uint32_t)ldy * 4u;            // bytes per row of y
-        const __amdgpu_buffer_rsrc_t yrs = make_rsrc(out, (uint32_t)M * rstride);
-        const uint32_t lane_row = (uint32_t)(4 * gq) * rstride;
+        for (int c = 0; c < KT; c += 3) {
+            ktile(c, sx0, sw1, sx2, sw2);
+            if (c + 1 < KT)
+                ktile(c + 1, sx1, sw2, sx0, sw0);
+            if (c + 2 < KT)
+                ktile(c + 2, sx2, sw0, sx1, sw1);
+        }
+
+        // ---- add the k-halves ------------------------------------------------------
+        // Wave kh finishes row-block positions 4kh..4kh+3 of its whole tiles and
+        // the kh-th half of its remaining-tile blocks.  Both waves of a pair hand
+        // the partner the half it finishes, all through LDS at once: fragment f
+        // (64 lanes x 16 bytes) of wave v sits in its own slot of the now free
+        // stage buffers, so one barrier separates the writes from the reads, and
+        // both waves of a SIMD then share the epilogue.
+        constexpr int HR = RR / 2;                                 // remaining blocks kept per wave
+        constexpr int kKeep = 4 * Q + RB * HR;                     // fragments kept (and handed over)
+        static_assert(kKeep <= 8 || 2 * (kKeep - 8 < 8 ? kKeep - 8 : 8) * 1024 <= kWStageBytes,
+                      "fragments 8..15 of waves 4..7: two waves per weight stage");
+        static_assert(kKeep <= 16 || (kKeep <= 18 && 8 * 2048 <= kWStageBytes),
+                      "fragments 16, 17: the third weight stage");
+        static_assert(3 * (kXStageBytes + kWStageBytes) + kBM * 4 <= 160 * 1024, "LDS of one CU");
+        floatx4_t keep[kKeep > 0 ? kKeep : 1];
+        {
+            // every wave is past its last LDS read of the stages (the last
+            // compute ended with them) and its trailing zero-writing loads have
+            // landed, so the stage buffers are free
+            __builtin_amdgcn_s_waitcnt(kWaitVm0);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_s_barrier();
+            auto slot = [&](int v, int f) __attribute__((always_inline)) {
+                uint8_t *base;
+                if (f < 8)
+                    base = (v < 4 ? sx0 : sx1) + (v & 3) * 8192 + f * 1024;
+                else if (f < 16)
+                    base = v < 4 ? sx2 + v * 8192 + (f - 8) * 1024
+                                 : (v < 6 ? sw0 : sw1) + (v & 1) * (kKeep - 8 < 8 ? kKeep - 8 : 8) * 1024 + (f - 8) * 1024;
+                else
+                    base = sw2 + v * 2048 + (f - 16) * 1024;
+                return reinterpret_cast<floatx4_t *>(base) + lane;
+            };
+            const bool upper = kh != 0;
+#pragma unroll
+            for (int j = 0; j < Q; ++j)
+#pragma unroll
+                for (int ii = 0; ii < 4; ++ii) {
+                    const floatx4_t lo = accF[j][ii], hi = accF[j][ii + 4];
+                    *slot(wave, 4 * j + ii) = upper ? lo : hi;
+                    keep[4 * j + ii] = upper ? hi : lo;
+                }
+#pragma unroll
+            for (int j = 0; j < RB; ++j)
+#pragma unroll
+                for (int ii = 0; ii < HR; ++ii) {
+                    const floatx4_t lo = accR[j][ii], hi = accR[j][ii + HR];
+                    *slot(wave, 4 * Q + HR * j + ii) = upper ? lo : hi;
+                    keep[4 * Q + HR * j + ii] = upper ? hi : lo;
+                }
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_s_barrier();
+#pragma unroll
+            for (int f = 0; f < kKeep; ++f)
+                keep[f] += *slot(wave ^ 4, f);
+        }
+        // fragment f of keep: tile and 16-row block (wave-uniform)
+        auto frag_tile = [&](int f) __attribute__((always_inline)) {
+            return f < 4 * Q ? tile0 + w * Q + f / 4
+                             : tile0 + (RT == 2 ? 4 * Q + (w >> 1) : 4 * Q + (f - 4 * Q) / (HR > 0 ? HR : 1));
+        };
+        auto frag_block = [&](int f) __attribute__((always_inline)) {
+            return f < 4 * Q ? (4 * kh + f % 4) ^ rb : rb + HR * kh + (f - 4 * Q) % (HR > 0 ? HR : 1);
+        };
+        // output multipliers of rows 4gq..4gq+3 of 16-row block blk: g, or after
+        // an fp16 run g * 2^c of each row (which undoes the row's scaling exactly)
+        auto row_mul = [&](int blk) __attribute__((always_inline)) {
+            if constexpr (F16)
+                return *reinterpret_cast<const floatx4_t *>(srow + 16 * blk + 4 * gq);
+            else
+                return floatx4_t{g, g, g, g};
+        };
+
+        // ---- epilogue: lane (r, gq) holds rows 4*gq + i of each 16-row block ----
+        if (SILU) {
+            const bool hi = r >= 8;
+            if (buf_out) {
+                // bf16 h through buffer stores as y below (2 bytes per output, rows
+                // past M dropped at the buffer's end)
+                const uint32_t hstride = (uint32_t)ldy * 2u;        // bytes per row of h
+                const __amdgpu_buffer_rsrc_t hrs = make_rsrc(out, (uint32_t)M * hstride);
+                // lanes r < 8 write rows 4gq, 4gq+1 of a block, lanes r >= 8 rows
+                // 4gq+2, 4gq+3; output f = 8t + r%8
+                const uint32_t lane_row = (uint32_t)(4 * gq + (hi ? 2 : 0)) * hstride;
+#pragma unroll
+                for (int f = 0; f < kKeep; ++f) {
+                    const int t = frag_tile(f);
+                    if (t < NT) {
+                        const floatx4_t v = keep[f];
+                        const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+                        const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
+                        const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
+                        const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
+                        const floatx4_t gv = row_mul(frag_block(f));
+                        const float gma = hi ? gv[2] : gv[0], gmb = hi ? gv[3] : gv[1];
+                        const uint32_t fo = 8u * (uint32_t)t + (uint32_t)(r & 7);
+                        const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane(
+                            (int)((uint32_t)(m0 + 16 * frag_block(f)) * hstride));
+                        const uint32_t off = lane_row + fo * 2u + row;
+                        __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(gma * ga, gma * ua), hrs, (int)off, 0, 0);
+                        __builtin_amdgcn_raw_buffer_store_b16(silu_mul_bf16(gmb * gb, gmb * ub), hrs,
+                                                              (int)(off + hstride), 0, 0);
+                    }
+                }
+            } else {
+                // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
+                uint16_t *h = static_cast<uint16_t *>(out);
+#pragma unroll
+                for (int f = 0; f < kKeep; ++f) {
+                    const int t = frag_tile(f);
+                    if (t < NT) {
+                        const floatx4_t v = keep[f];
+                        const float v0 = v[0], v1 = v[1], v2 = v[2], v3 = v[3];
+                        const float s0 = swap8(v0), s1 = swap8(v1), s2 = swap8(v2), s3 = swap8(v3);
+                        const float ga = hi ? s2 : v0, ua = hi ? v2 : s0;
+                        const float gb = hi ? s3 : v1, ub = hi ? v3 : s1;
+                        const floatx4_t gv = row_mul(frag_block(f));
+                        const float gma = hi ? gv[2] : gv[0], gmb = hi ? gv[3] : gv[1];
+                        const int m = m0 + 16 * frag_block(f) + 4 * gq + (hi ? 2 : 0);
+                        const int64_t fo = 8 * (int64_t)t + (r & 7);
+                        if (m < M)
+                            h[(int64_t)m * ldy + fo] = silu_mul_bf16(gma * ga, gma * ua);
+                        if (m + 1 < M)
+                            h[(int64_t)(m + 1) * ldy + fo] = silu_mul_bf16(gmb * gb, gmb * ub);
+                    }
+                }
+            }
+            return;
+        }
+        if (buf_out) {
+            // y through buffer stores: the row part of each offset is wave-uniform
+            // and the lane part fixed, so a store costs one add.  Rows past M lie
+            // past the end of the buffer (buf_out: the launch's rows plus one block
+            // stay under 2 GiB of y) and are dropped by the hardware instead of
+            // being tested per store.
+            const uint32_t rstride = (uint32_t)ldy * 4u;            // bytes per row of y
+            const __amdgpu_buffer_rsrc_t yrs = make_rsrc(out, (uint32_t)M * rstride);
+            const uint32_t lane_row = (uint32_t)(4 * gq) * rstride;
+#pragma unroll
+            for (int f = 0; f < kKeep; ++f) {
+                const int t = frag_tile(f);
+                const int n = t * 16 + r;
+                if (t < NT && n < N) {
+                    const int mb = m0 + 16 * frag_block(f);
+                    const floatx4_t gv = row_mul(frag_block(f));
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(mb + e) * rstride));
+                        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, gv[e] * keep[f][e]), yrs,
+                                                              (int)(lane_row + (uint32_t)n * 4u + row), 0, 0);
+                    }
+                }
+            }
+            return;
+        }
+        // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
+        float *y = static_cast<float *>(out);
 #pragma unroll
         for (int f = 0; f < kKeep; ++f) {
             const int t = frag_tile(f);
             const int n = t * 16 + r;
             if (t < NT && n < N) {
-                const int mb = m0 + 16 * frag_block(f);
+                const int mb = m0 + 16 * frag_block(f) + 4 * gq;
+                const floatx4_t gv = row_mul(frag_block(f));
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
-                    const uint32_t row = (uint32_t)__builtin_amdgcn_readfirstlane((int)((uint32_t)(mb + e) * rstride));
-                    __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, g * keep[f][e]), yrs,
-                                                          (int)(lane_row + (uint32_t)n * 4u + row), 0, 0);
+                    const int m = mb + e;
+                    if (m < M)
+                        y[(int64_t)m * ldy + n] = gv[e] * keep[f][e];
                 }
             }
         }
-        return;
+    };
+
+    // The block's 128 row multipliers, two per lane (rows past M read zero),
+    // then the weight loads of stages 0 and 1, which do not depend on the
+    // operand type.  The multipliers return first: fp16 operands when the
+    // activations were staged (xh) and none of the block's rows is marked
+    // inexact (NaN), else bf16.  Every wave holds the same 128 multipliers,
+    // so the decision is the workgroup's.
+    float rm0 = 0.f, rm1 = 0.f;
+    if (xh != nullptr) {
+        const __amdgpu_buffer_rsrc_t rs = make_rsrc(rowmul, (uint32_t)M * 4u);
+        rm0 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs, (int)((uint32_t)(m0 + lane) * 4u), 0, 0));
+        rm1 = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                           rs, (int)((uint32_t)(m0 + 64 + lane) * 4u), 0, 0));
     }
-    // outputs past 2 GiB of 32-bit offsets: plain stores, rows tested
-    float *y = static_cast<float *>(out);
-#pragma unroll
-    for (int f = 0; f < kKeep; ++f) {
-        const int t = frag_tile(f);
-        const int n = t * 16 + r;
-        if (t < NT && n < N) {
-            const int mb = m0 + 16 * frag_block(f) + 4 * gq;
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int m = mb + e;
-                if (m < M)
-                    y[(int64_t)m * ldy + n] = g * keep[f][e];
-            }
+    issue_wstage(0, true, sw0);
+    issue_wstage(1, KT > 1, sw1);
+    static_assert(kLoads < 16, "vmcnt immediate");
+    const bool f16 = xh != nullptr &&
+                     __builtin_amdgcn_ballot_w64(__builtin_isnan(rm0) || __builtin_isnan(rm1)) == 0;
+    if (f16) {
+        // the epilogue's copy (read after the k-loop's barriers)
+        if (wave == 0) {
+            srow[lane] = rm0;
+            srow[64 + lane] = rm1;
         }
+        run(std::true_type{}, xh);
+    } else {
+        run(std::false_type{}, x);
     }
 }
 
-typedef void (*gemm_fn)(const uint8_t *, const uint8_t *, float, const uint16_t *, void *, int, int,
-                        int64_t, int, int, int, int);
+// ---- fp16 staging of the activations ----------------------------------------
+// Row m of x (K bf16 values) is written to xh as fp16 values scaled by 2^-c,
+// with c = E - 15 for E the largest exponent (floor(log2|v|)) among the row's
+// nonzero values: every value of the row then lies below 2^16 and converts
+// exactly as long as the smallest nonzero one stays at or above fp16's
+// smallest normal 2^-14, i.e. when the row spans at most 29 binades (bf16
+// carries 8 significant bits, fp16 11).  rowmul[m] = g * 2^c, the factor
+// that turns the row's fp32 sums back into g times the unscaled sums
+// exactly; it is NaN when the row would not convert exactly, holds an
+// infinity or a NaN, or g * 2^c is not a normal float (or g is not finite),
+// and the GEMM then runs the bf16 loop for that row's block.
+// One wave per row (four rows per 256-thread workgroup); K % 8 == 0.
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// floor(log2 v) of the nonzero finite bf16 magnitude with bit pattern a
+__device__ __forceinline__ int bf16_exponent(uint32_t a)
+{
+    const uint32_t e = a >> 7;
+    return e ? (int)e - 127 : (31 - __builtin_clz(a & 0x7fu)) - 133;
+}
+
+__global__ void __launch_bounds__(256)
+gemm_xprep_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K, float g,
+                  uint16_t *__restrict__ xh, float *__restrict__ rowmul)
+{
+    // 16-byte chunks (8 values) of the row: lane l takes chunks l, l + 64,
+    // ...; the first kHeld of them stay in registers between the two passes
+    // (rows up to K = 8192), the rest are read again.  Buffer accesses past
+    // the row read zero / are dropped.
+    constexpr int kHeld = 16;
+    const int64_t m = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+    if (m >= M)
+        return;
+    const uint32_t lane = threadIdx.x & 63;
+    const uint32_t row_bytes = (uint32_t)(K * 2);
+    const __amdgpu_buffer_rsrc_t xs = make_rsrc(x + m * K, row_bytes);
+    const __amdgpu_buffer_rsrc_t hs = make_rsrc(xh + m * K, row_bytes);
+    auto load = [&](uint32_t chunk) __attribute__((always_inline)) {
+        return __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xs, (int)(chunk * 16u), 0, 0));
+    };
+    // largest magnitude and smallest nonzero magnitude as bf16 bit patterns
+    // (ordered like the values): packed 16-bit max of |v| and min of |v| - 1
+    // (zero wraps to 0xffff)
+    u16x2_t amax = {0, 0}, amin1 = {0xffff, 0xffff};
+    auto scan = [&](const u32x4_t &v) __attribute__((always_inline)) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const u16x2_t a = __builtin_bit_cast(u16x2_t, v[i] & 0x7fff7fffu);
+            amax = __builtin_elementwise_max(amax, a);
+            amin1 = __builtin_elementwise_min(amin1, a - (u16x2_t){1, 1});
+        }
+    };
+    const uint32_t nchunks = (uint32_t)(K / 8);
+    u32x4_t held[kHeld];
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i)
+        held[i] = load(lane + 64u * i);
+#pragma unroll
+    for (int i = 0; i < kHeld; ++i)
+        scan(held[i]);
+    for (uint32_t ch = lane + 64u * kHeld; ch < nchunks; ch += 64u)
+        scan(load(ch));
+    uint32_t hi_bits = amax[0] > amax[1] ? amax[0] : amax[1];
+    uint32_t lo_bits1 = amin1[0] < amin1[1] ? amin1[0] : amin1[1];
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+        const uint32_t h2 = (uint32_t)__shfl_xor((int)hi_bits, off, 64);
+        const uint32_t l2 = (uint32_t)__shfl_xor((int)lo_bits1, off, 64);
+        hi_bits = h2 > hi_bits ? h2 : hi_bits;
+        lo_bits1 = l2 < lo_bits1 ? l2 : lo_bits1;
+    }
+    const bool nonfinite = hi_bits >= 0x7f80u;
+    const bool zero_row = hi_bits == 0;
+    const int c = zero_row || nonfinite ? 0 : bf16_exponent(hi_bits) - 15;
+    const bool exact = zero_row || (!nonfinite && bf16_exponent(lo_bits1 + 1) - c >= -14);
+    auto convert_store = [&](const u32x4_t &v, uint32_t chunk) __attribute__((always_inline)) {
+        u32x4_t o;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float f0 = __builtin_bit_cast(float, v[i] << 16);
+            const float f1 = __builtin_bit_cast(float, v[i] & 0xffff0000u);
+            const f16x2_t hh = {(_Float16)__builtin_ldexpf(f0, -c), (_Float16)__builtin_ldexpf(f1, -c)};
+            o[i] = __builtin_bit_cast(uint32_t, hh);
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4_t, o), hs, (int)(chunk * 16u), 0, 0);
+    };
+    // rows that take the bf16 loop need no fp16 copy
+    if (exact) {
+#pragma unroll
+        for (int i = 0; i < kHeld; ++i)
+            convert_store(held[i], lane + 64u * i);
+        for (uint32_t ch = lane + 64u * kHeld; ch < nchunks; ch += 64u)
+            convert_store(load(ch), ch);
+    }
+    if (lane == 0) {
+        const float gm = __builtin_ldexpf(g, c);
+        const float agm = __builtin_fabsf(gm);
+        const bool mul_ok = g == 0.0f || (agm >= 1.17549435e-38f && agm <= 3.40282347e+38f);
+        rowmul[m] = exact && mul_ok ? gm : __builtin_nanf("");
+    }
+}
+
+typedef void (*gemm_fn)(const uint8_t *, const uint8_t *, float, const uint16_t *, const uint16_t *,
+                        const float *, void *, int, int, int64_t, int, int, int, int);
 
 #define Q4P_GEMM_ENTRY(T) gemm_kernel<(T) / 4, (T) % 4, false>
 const gemm_fn kGemmTable[kMaxT + 1] = {
@@ -554,13 +761,28 @@ const gemm_fn kGemmSiluTable[kMaxT + 1] = {
 };
 #undef Q4P_GEMM_ENTRY
 
-// out: fp32 y[M][N], or with silu bf16 h[M][N/2] (N = 2F, fused gate/up)
+int64_t align256(int64_t n) { return (n + 255) / 256 * 256; }
+
+// out: fp32 y[M][N], or with silu bf16 h[M][N/2] (N = 2F, fused gate/up).
+// workspace (or null: bf16 operands throughout): gemm_workspace_bytes(M, K)
+// bytes, 16-byte aligned: the fp16 activations, then the row multipliers.
 hipError_t launch_gemm_any(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                            const uint16_t *x, void *out, int64_t M, int64_t N, int64_t K,
-                           bool silu, hipStream_t stream)
+                           bool silu, void *workspace, hipStream_t stream)
 {
     const int64_t NT = n_tiles(N);
     const int64_t KT = k_tiles(K);
+    uint16_t *xh = nullptr;
+    float *rowmul = nullptr;
+    if (workspace) {
+        xh = static_cast<uint16_t *>(workspace);
+        rowmul = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + align256(M * K * 2));
+        hipLaunchKernelGGL(gemm_xprep_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, x,
+                           M, K, g, xh, rowmul);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
     // Buffer offsets are 32-bit: one launch covers at most 1 GiB of
     // activations and of packed codes; larger problems run as several
     // launches over row and tile ranges (y keeps its row stride N).
@@ -594,7 +816,8 @@ hipError_t launch_gemm_any(const uint8_t *packed_codes, const uint8_t *packed_sc
             const int buf_out = (Mc + kBM) * row_bytes <= (int64_t(1) << 31) ? 1 : 0;
             hipLaunchKernelGGL(silu ? kGemmSiluTable[T] : kGemmTable[T], grid, block, 0, stream,
                                packed_codes + tb * KT * kTileCodeBytes,
-                               packed_scales + tb * KT * kTileScaleBytes, g, x + mb * K, o,
+                               packed_scales + tb * KT * kTileScaleBytes, g, x + mb * K,
+                               xh ? xh + mb * K : nullptr, rowmul ? rowmul + mb : nullptr, o,
                                (int)Mc, (int)Nc, silu ? N / 2 : N, (int)K, (int)KT, (int)NTc,
                                buf_out);
             const hipError_t e = hipGetLastError();
@@ -607,18 +830,24 @@ hipError_t launch_gemm_any(const uint8_t *packed_codes, const uint8_t *packed_sc
 
 }  // namespace
 
+size_t gemm_workspace_bytes(int64_t M, int64_t K)
+{
+    return (size_t)(align256(M * K * 2) + align256(M * 4));
+}
+
 hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream)
+                       void *workspace, hipStream_t stream)
 {
-    return launch_gemm_any(packed_codes, packed_scales, g, x, y, M, N, K, false, stream);
+    return launch_gemm_any(packed_codes, packed_scales, g, x, y, M, N, K, false, workspace, stream);
 }
 
 hipError_t launch_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
                                 float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
-                                int64_t K, hipStream_t stream)
+                                int64_t K, void *workspace, hipStream_t stream)
 {
-    return launch_gemm_any(packed_codes, packed_scales, g, x, h, M, 2 * F, K, true, stream);
+    return launch_gemm_any(packed_codes, packed_scales, g, x, h, M, 2 * F, K, true, workspace,
+                           stream);
 }
 
 }  // namespace q4p

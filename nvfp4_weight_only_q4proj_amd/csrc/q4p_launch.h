@@ -58,14 +58,19 @@ hipError_t launch_gemv_argmax(const uint8_t *packed_codes, const uint8_t *packed
                               int64_t M, int64_t N, int64_t K, void *workspace,
                               hipStream_t stream);
 
+// GEMM workspace: the fp16 copy of the activations and the per-row output
+// multipliers (no initial contents; left holding them).  A null workspace
+// runs the bf16 operand path.
+size_t gemm_workspace_bytes(int64_t M, int64_t K);
+
 hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream);
+                       void *workspace, hipStream_t stream);
 
 // The fused gate/up projection + silu(gate)*up for any M (F % 8 == 0).
 hipError_t launch_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
                                 float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
-                                int64_t K, hipStream_t stream);
+                                int64_t K, void *workspace, hipStream_t stream);
 
 // NVFP4 quantizer: bf16 W [N][K] -> canonical codes, scales, global scale
 // (device float).  workspace: quant_workspace_bytes(), no initial contents.

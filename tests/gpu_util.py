@@ -40,8 +40,13 @@ def project(kind: str, packed, g: float, x: np.ndarray, N: int, K: int) -> np.nd
     M = x.shape[0]
     xd = to_dev_x(x)
     y = torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV)
-    fn = m.q4proj_gemv if kind == "gemv" else m.q4proj_gemm
-    fn(packed[0], packed[1], g, xd, y, M, N, K)
+    if kind == "gemv":
+        m.q4proj_gemv(packed[0], packed[1], g, xd, y, M, N, K)
+    else:
+        # "gemm": fp16 operands (the binding's GEMM scratch); "gemm_bf16": no
+        # workspace, bf16 operands
+        m.q4proj_gemm(packed[0], packed[1], g, xd, y, M, N, K,
+                      workspace=False if kind == "gemm_bf16" else None)
     torch.cuda.synchronize()
     return y.cpu().numpy()
 

@@ -189,6 +189,41 @@ static void gemm_checks(void)
     REJECT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(X, 64), 512, N, K, NULL, 0,
                        STREAM),
            Q4P_EINVAL, "gemm y overlaps x");
+    CHECK(stub_last()->workspace == NULL, "gemm without a workspace: NULL passed on");
+
+    /* the optional fp16-staging workspace: 2MK and 4M bytes, each rounded up to 256 */
+    const size_t need = q4proj_gemm_workspace_bytes(512, N, K);
+    CHECK(need == 5242880u + 2048u, "gemm workspace size %zu", need);
+    CHECK(q4proj_gemm_workspace_bytes(3, N, 16) == 256u + 256u, "gemm workspace rounding");
+    CHECK(q4proj_gemm_workspace_bytes(0, N, K) == 0 && q4proj_gemm_workspace_bytes(1, N, 1041) == 0 &&
+              q4proj_gemm_workspace_bytes(((int64_t)1 << 24) + 1, N, K) == 0 &&
+              q4proj_gemm_workspace_bytes(1, 0, K) == 0,
+          "gemm workspace size of invalid arguments");
+    ACCEPT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, VP(WS, 0), need,
+                       STREAM),
+           "gemm", "gemm with a workspace");
+    CHECK(stub_last()->workspace == VP(WS, 0), "gemm workspace not passed on");
+    ACCEPT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, NULL, 12345,
+                       STREAM),
+           "gemm", "gemm: workspace_bytes ignored without a workspace");
+    REJECT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, VP(WS, 0),
+                       need - 1, STREAM),
+           Q4P_EWORKSPACE, "gemm workspace one byte short");
+    REJECT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, VP(WS, 8), need,
+                       STREAM),
+           Q4P_EINVAL, "gemm workspace misaligned");
+    REJECT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, VP(X, 4096),
+                       need, STREAM),
+           Q4P_EINVAL, "gemm workspace overlaps x");
+    REJECT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, VP(Y, 0), need,
+                       STREAM),
+           Q4P_EINVAL, "gemm workspace overlaps y");
+    REJECT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, VP(PC, 1024),
+                       need, STREAM),
+           Q4P_EINVAL, "gemm workspace overlaps the packed codes");
+    REJECT(q4proj_gemm(U8(PC, 0), U8(PS, 0), 2.f, U16(X, 0), F32(Y, 0), 512, N, K, VP(PS, 0), need,
+                       STREAM),
+           Q4P_EINVAL, "gemm workspace overlaps the packed scales");
 }
 
 static void pack_checks(void)
@@ -262,6 +297,22 @@ static void silu_argmax_quant_checks(void)
     ACCEPT(q4proj_gemm_silu_mul(U8(PC, 0), U8(PS, 0), 1.f, U16(X, 0), U16(Y, 0), 512, F, K, NULL, 0,
                                 STREAM),
            "gemm_silu_mul", "gemm_silu_mul");
+    {
+        const size_t need = q4proj_gemm_workspace_bytes(512, 2 * F, K);
+        ACCEPT(q4proj_gemm_silu_mul(U8(PC, 0), U8(PS, 0), 1.f, U16(X, 0), U16(Y, 0), 512, F, K,
+                                    VP(WS, 0), need, STREAM),
+               "gemm_silu_mul", "gemm_silu_mul with a workspace");
+        CHECK(stub_last()->workspace == VP(WS, 0), "gemm_silu_mul workspace not passed on");
+        REJECT(q4proj_gemm_silu_mul(U8(PC, 0), U8(PS, 0), 1.f, U16(X, 0), U16(Y, 0), 512, F, K,
+                                    VP(WS, 0), need - 256, STREAM),
+               Q4P_EWORKSPACE, "gemm_silu_mul workspace short");
+        REJECT(q4proj_gemm_silu_mul(U8(PC, 0), U8(PS, 0), 1.f, U16(X, 0), U16(Y, 0), 512, F, K,
+                                    VP(Y, 64), need, STREAM),
+               Q4P_EINVAL, "gemm_silu_mul workspace overlaps h");
+        REJECT(q4proj_gemm_silu_mul(U8(PC, 0), U8(PS, 0), 1.f, U16(X, 0), U16(Y, 0), 512, F, K,
+                                    VP(WS, 4), need, STREAM),
+               Q4P_EINVAL, "gemm_silu_mul workspace misaligned");
+    }
 
     ACCEPT(q4proj_gemv_argmax(U8(PC, 0), U8(PS, 0), 1.f, U16(X, 0), NULL, F32(V, 0), I64(IDX, 0), 1,
                               N, K, VP(WS, 0), 12288, STREAM),

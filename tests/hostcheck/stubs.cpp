@@ -192,20 +192,27 @@ hipError_t launch_gemv_argmax(const uint8_t *packed_codes, const uint8_t *packed
                   stream, g);
 }
 
+// the documented size: the fp16 activations and the row multipliers, each
+// rounded up to 256 bytes
+size_t gemm_workspace_bytes(int64_t M, int64_t K)
+{
+    return (size_t)((M * K * 2 + 255) / 256 * 256 + (M * 4 + 255) / 256 * 256);
+}
+
 hipError_t launch_gemm(const uint8_t *packed_codes, const uint8_t *packed_scales, float g,
                        const uint16_t *x, float *y, int64_t M, int64_t N, int64_t K,
-                       hipStream_t stream)
+                       void *workspace, hipStream_t stream)
 {
     (void)x;
-    return record("gemm", M, N, K, packed_codes, packed_scales, y, nullptr, stream, g);
+    return record("gemm", M, N, K, packed_codes, packed_scales, y, workspace, stream, g);
 }
 
 hipError_t launch_gemm_silu_mul(const uint8_t *packed_codes, const uint8_t *packed_scales,
                                 float g, const uint16_t *x, uint16_t *h, int64_t M, int64_t F,
-                                int64_t K, hipStream_t stream)
+                                int64_t K, void *workspace, hipStream_t stream)
 {
     (void)x;
-    return record("gemm_silu_mul", M, F, K, packed_codes, packed_scales, h, nullptr, stream, g);
+    return record("gemm_silu_mul", M, F, K, packed_codes, packed_scales, h, workspace, stream, g);
 }
 
 size_t quant_workspace_bytes() { return g_quant_ws; }

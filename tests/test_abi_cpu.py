@@ -25,7 +25,7 @@ def declared_functions():
 
 def test_exports_every_declared_symbol(q4):
     names = declared_functions()
-    assert len(names) == 18, names
+    assert len(names) == 19, names
     lib = q4.library()
     for name in names:
         assert hasattr(lib, name), name
@@ -47,51 +47,73 @@ def test_packed_sizes(q4, N, K):
     assert q4.q4proj_packed_codes_bytes(N, K) == nt * kt * 1024 >= N * K // 2
     assert q4.q4proj_packed_scales_bytes(N, K) == nt * kt * 128 >= N * K // 16
     # gemv's exchange words: one 64-bit word x 4 rows x 64 lanes per workgroup
-    # boundary (256 at most), plus, when K is cut into KS ranges so that a
-    # range's activations (M x k-tiles x 256 B) fit in 128 KiB, one word per
-    # output for each of the KS - 1 joins
+    # boundary (256 at most), plus one word per output for each of the KS - 1
+    # joins when K is cut into KS ranges; a range's activations (M x k-tiles
+    # x 256 B / KS) must fit in the 147,392 staging bytes, and which of the
+    # counts that fit is taken is the library's estimate (M = 1 takes one
+    # range up to K = 65536; the verify shape M = 7, K = 17408 four)
     for M in (1, 7, 16):
-        ks = 1
-        while ks < 8 and M * -(-kt // ks) * 256 > 128 * 1024:
-            ks *= 2
-        assert q4.q4proj_workspace_bytes(M, N, K) == 512 * 1024 + 8 * (ks - 1) * M * N
+        got = q4.q4proj_workspace_bytes(M, N, K)
+        extra = got - 512 * 1024
+        assert extra >= 0 and extra % (8 * M * N) == 0, (M, got)
+        ks = extra // (8 * M * N) + 1
+        assert ks in (1, 2, 4, 8) and M * -(-kt // ks) * 256 <= 147392, (M, ks)
+        if M == 1:
+            assert ks == 1
+        if (M, N, K) == (7, 5120, 17408):
+            assert ks == 4
     assert q4.q4proj_workspace_bytes(17, N, K) == 0
     assert q4.q4proj_workspace_bytes(512, N, K) == 0
+    # the GEMMs' optional staging workspace: 2MK and 4M bytes, each rounded
+    # up to 256
+    for M in (1, 7, 512, 513):
+        r256 = lambda n: -(-n // 256) * 256
+        assert q4.q4proj_gemm_workspace_bytes(M, N, K) == r256(2 * M * K) + r256(4 * M)
 
 
 def test_workspace_of_the_verify_shape(q4):
-    # M = 7 at K = 17408: 244 KB of activations -> two K ranges, one join
-    assert q4.q4proj_workspace_bytes(7, 5120, 17408) == 512 * 1024 + 8 * 7 * 5120
+    # M = 7 at K = 17408 (down, 244 KB of activations): four K ranges, three
+    # joins; at K = 5120 (gate/up) one range
+    assert q4.q4proj_workspace_bytes(7, 5120, 17408) == 512 * 1024 + 3 * 8 * 7 * 5120
     assert q4.q4proj_workspace_bytes(7, 17408, 5120) == 512 * 1024
 
 
-def silu_ranges(M, K):
-    """K ranges of the fused gate/up GEMV, as for the plain GEMV: the fewest
-    of 1, 2, 4, 8 whose activations (M x k-tiles x 256 B) stay within 128 KiB
-    (None: not served)."""
+def fitting_ranges(M, K):
+    """K range counts (1, 2, 4, 8, none of them empty) whose activations,
+    M x k-tiles-per-range x 256 B, fit in the 147,392 staging bytes."""
     kt = -(-K // 128)
-    ks = 1
-    while ks < 8 and M * -(-kt // ks) * 256 > 128 * 1024:
-        ks *= 2
-    return ks if M * -(-kt // ks) * 256 <= 128 * 1024 else None
+    out = []
+    for ks in (1, 2, 4, 8):
+        ktr = -(-kt // ks)
+        if kt - (ks - 1) * ktr < 1:
+            break
+        if M * ktr * 256 <= 147392:
+            out.append(ks)
+    return out
 
 
 @pytest.mark.parametrize("M", [1, 2, 7, 12, 13, 16])
 @pytest.mark.parametrize("F,K", [(16, 16), (17408, 5120), (8192, 8192), (4096, 17408),
                                  (64, 32768), (64, 65536), (64, 262144)])
 def test_silu_mul_workspace(q4, M, F, K):
-    ks = silu_ranges(M, K)
-    want = 0 if ks is None else 8 * (65536 + (ks - 1) * M * F)
-    assert q4.q4proj_silu_mul_workspace_bytes(M, F, K) == want
+    # served exactly when some range count fits; the workspace then holds the
+    # boundary words plus M x F words per join of the count taken
+    fits = fitting_ranges(M, K)
+    got = q4.q4proj_silu_mul_workspace_bytes(M, F, K)
+    if not fits:
+        assert got == 0
+        return
+    extra = got - 8 * 65536
+    assert extra >= 0 and extra % (8 * M * F) == 0, got
+    assert extra // (8 * M * F) + 1 in fits
 
 
 def test_silu_mul_workspace_limits(q4):
-    # one range up to 128 KiB of activations (M x k-tiles = 512), two above
-    assert q4.q4proj_silu_mul_workspace_bytes(8, 64, 64 * 128) == 8 * 65536
-    assert q4.q4proj_silu_mul_workspace_bytes(8, 64, 65 * 128) == 8 * (65536 + 8 * 64)
-    assert q4.q4proj_silu_mul_workspace_bytes(1, 8, 128) == 8 * 65536
-    assert q4.q4proj_silu_mul_workspace_bytes(16, 64, 32768) > 0
-    assert q4.q4proj_silu_mul_workspace_bytes(16, 64, 32768 + 128) == 0
+    # M = 16 is served while 16 x ceil(k-tiles / 8) x 256 <= 147,392 B, i.e.
+    # up to 280 k-tiles
+    assert q4.q4proj_silu_mul_workspace_bytes(16, 64, 280 * 128) > 0
+    assert q4.q4proj_silu_mul_workspace_bytes(16, 64, 281 * 128) == 0
+    assert q4.q4proj_silu_mul_workspace_bytes(1, 8, 128) == 8 * 65536     # one k-tile: one range
     for M, F, K in [(0, 16, 128), (17, 16, 128), (1, 4, 128), (1, 12, 128), (1, 0, 128),
                     (1, 16, 120), (1, 16, 0)]:
         assert q4.q4proj_silu_mul_workspace_bytes(M, F, K) == 0, (M, F, K)
@@ -142,6 +164,23 @@ def test_gemv_workspace_validation(q4):
     assert proj(lib, "q4proj_gemv", ws=X) == q4.EINVAL           # overlaps x
 
 
+def test_gemm_workspace_validation(q4):
+    # the optional staging workspace of the GEMMs: big enough, 16-byte
+    # aligned, apart from every other argument
+    lib = q4.library()
+    need = q4.q4proj_gemm_workspace_bytes(512, 64, 256)
+    assert need == 2 * 512 * 256 + 2048
+    assert proj(lib, "q4proj_gemm", M=512, wsb=need - 1) == q4.EWORKSPACE
+    assert proj(lib, "q4proj_gemm", M=512, ws=W + 8, wsb=need) == q4.EINVAL
+    assert proj(lib, "q4proj_gemm", M=512, ws=X + 4096, wsb=need) == q4.EINVAL   # overlaps x
+    assert proj(lib, "q4proj_gemm", M=512, ws=Y - 4096, wsb=need) == q4.EINVAL   # overlaps y
+    assert proj(lib, "q4proj_gemm", M=512, ws=A, wsb=need) == q4.EINVAL          # packed codes
+    assert silu(lib, fn="q4proj_gemm_silu_mul", M=512, wsb=need - 1) == q4.EWORKSPACE
+    assert silu(lib, fn="q4proj_gemm_silu_mul", M=512, ws=Y, wsb=need) == q4.EINVAL  # overlaps h
+    assert q4.q4proj_gemm_workspace_bytes(0, 64, 256) == 0
+    assert q4.q4proj_gemm_workspace_bytes(1, 64, 250) == 0
+
+
 def test_gemv_m_range(q4):
     lib = q4.library()
     assert proj(lib, "q4proj_gemv", M=17) == q4.EUNSUPPORTED
@@ -163,7 +202,7 @@ def test_silu_mul_validation(q4):
     for kw in SILU_BAD + [dict(ws=None), dict(ws=W + 4), dict(ws=Y - 4096), dict(ws=X)]:
         assert silu(lib, **kw) == q4.EINVAL, kw
     assert silu(lib, M=17) == q4.EUNSUPPORTED
-    assert silu(lib, M=16, K=32768 + 128) == q4.EUNSUPPORTED
+    assert silu(lib, M=16, K=281 * 128) == q4.EUNSUPPORTED
     assert silu(lib, wsb=WSB - 8) == q4.EWORKSPACE
     assert silu(lib, ws=None, wsb=0) == q4.EWORKSPACE
     for kw in SILU_BAD:
@@ -175,8 +214,9 @@ def test_argmax_validation(q4):
     need = q4.q4proj_argmax_workspace_bytes(1, 64, 256)
     assert need == 512 * 1024 + 16
     assert q4.q4proj_argmax_workspace_bytes(17, 64, 256) == 0
-    assert q4.q4proj_argmax_workspace_bytes(16, 64, 32768 + 128) == 0
-    assert q4.q4proj_argmax_workspace_bytes(7, 5120, 17408) == 512 * 1024 + 8 * 7 * 5120 + 64
+    assert q4.q4proj_argmax_workspace_bytes(16, 64, 281 * 128) == 0
+    # the gemv workspace of the shape (four K ranges here) plus 8 * (M + 1) bytes
+    assert q4.q4proj_argmax_workspace_bytes(7, 5120, 17408) == 512 * 1024 + 3 * 8 * 7 * 5120 + 64
     V, I = W + (1 << 20), W + (1 << 20) + 4096
 
     def am(pc=A, ps=B, x=X, y=Y, val=V, idx=I, M=1, N=64, K=256, ws=W, wsb=need):
@@ -189,7 +229,7 @@ def test_argmax_validation(q4):
                dict(ws=None), dict(ws=W + 4), dict(ws=X), dict(ws=V - 64)]:
         assert am(**kw) == q4.EINVAL, kw
     assert am(M=17) == q4.EUNSUPPORTED
-    assert am(M=16, K=32768 + 128) == q4.EUNSUPPORTED
+    assert am(M=16, K=281 * 128) == q4.EUNSUPPORTED
     assert am(wsb=need - 8) == q4.EWORKSPACE
     assert am(ws=None, wsb=0) == q4.EWORKSPACE
 
@@ -273,7 +313,8 @@ def test_no_device_no_fallback(q4):
     lib = q4.library()
     assert proj(lib, "q4proj_gemv") == q4.EDEVICE
     assert proj(lib, "q4proj_gemm", M=512) == q4.EDEVICE
-    assert proj(lib, "q4proj_gemm", M=512, ws=None, wsb=0) == q4.EDEVICE   # gemm needs none
+    assert proj(lib, "q4proj_gemm", M=512, ws=None, wsb=0) == q4.EDEVICE   # workspace optional
+    assert proj(lib, "q4proj_gemm", M=512, ws=None, wsb=123) == q4.EDEVICE
     assert lib.q4proj_pack(A, B, 16, 128, X, Y, None) == q4.EDEVICE
     assert lib.q4proj_gemv_noalloc(A, B, ctypes.c_float(1.0), X, Y, 1, 64, 256, None) == q4.EDEVICE
     assert lib.q4proj_pack_gate_up(A, B, A + 65536, B + 65536, ctypes.c_float(0.5),

@@ -3,8 +3,8 @@
 The FlashRT "Qwen3.6 NVFP4 usage" page's constructor-argument table has the
 runner pre-allocate every per-step buffer so that no call allocates and the
 decode step can be captured as a graph.  Here one graph holds the decode GEMV
-(M = 1), the verify GEMV (M = 7 with K = 17408: two K ranges joined through
-the workspace), the GEMM, the fused gate/up GEMV, the lm-head-style argmax
+(M = 1), the verify GEMV (M = 7 with K = 17408: K ranges joined through the
+workspace), the GEMM, the fused gate/up GEMV, the lm-head-style argmax
 (no logits) and the quantizer, each with a caller-provided workspace.  The
 graph is replayed several times; before each replay new activations and a new
 bf16 weight are copied into its input buffers and the device synchronised
@@ -52,7 +52,10 @@ def test_graph_replays_match_eager_bit_for_bit():
           "lm": torch.zeros(m.q4proj_argmax_workspace_bytes(1, 5000, 256), dtype=torch.uint8,
                             device=DEV),
           "quant": torch.zeros(m.q4proj_quantize_workspace_bytes(Nq, Kq), dtype=torch.uint8,
-                               device=DEV)}
+                               device=DEV),
+          # the GEMM's fp16 staging scratch (no contents required)
+          "pre": torch.empty(m.q4proj_gemm_workspace_bytes(40, 272, 1024), dtype=torch.uint8,
+                             device=DEV)}
 
     def outputs():
         return {"dec": torch.full((1, 1040), float("nan"), device=DEV),
@@ -70,7 +73,8 @@ def test_graph_replays_match_eager_bit_for_bit():
                       workspace=ws["dec"])
         m.q4proj_gemv(ver_w[0], ver_w[1], ver_mat.g, xs["ver"], o["ver"], 7, 640, 17408,
                       workspace=ws["ver"])
-        m.q4proj_gemm(pre_w[0], pre_w[1], pre_mat.g, xs["pre"], o["pre"], 40, 272, 1024)
+        m.q4proj_gemm(pre_w[0], pre_w[1], pre_mat.g, xs["pre"], o["pre"], 40, 272, 1024,
+                      workspace=ws["pre"])
         m.q4proj_gemv_silu_mul(mlp_w[0], mlp_w[1], mlp_mat.g, xs["mlp"], o["mlp"], 1, F, Kf,
                                workspace=ws["mlp"])
         m.q4proj_gemv_argmax(lm_w[0], lm_w[1], lm_mat.g, xs["lm"], None, o["val"], o["idx"],
@@ -120,5 +124,5 @@ def test_graph_replays_match_eager_bit_for_bit():
             assert bad == 0
     # the workspaces are left zero-filled by every call, replays included
     for k, w in ws.items():
-        if k != "quant":
+        if k not in ("quant", "pre"):
             assert int(torch.count_nonzero(w)) == 0, f"{k} workspace not left zero-filled"

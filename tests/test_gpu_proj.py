@@ -19,7 +19,7 @@ from gpu_util import (DEV, assert_parity, bits, note, oracle_fp32, pack, project
 
 pytestmark = pytest.mark.gpu
 
-KINDS = ["gemv", "gemm"]
+KINDS = ["gemv", "gemm", "gemm_bf16"]     # gemm: fp16 operands, gemm_bf16: without a workspace
 
 
 def same_values(a, b):
@@ -111,6 +111,7 @@ RAGGED = {
     "gemm": [(129, 300, 1040), (513, 100, 272), (1, 17, 5136), (200, 4112, 128),
              (64, 2049, 400), (300, 48, 2000)],
 }
+RAGGED["gemm_bf16"] = RAGGED["gemm"]
 
 
 @pytest.mark.parametrize("kind", KINDS)
