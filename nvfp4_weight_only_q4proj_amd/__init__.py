@@ -291,10 +291,24 @@ def gemm_scratch(device, nbytes: int, stream=None):
     return ws
 
 
+def gemm_staging_pays(M: int, N: int, K: int) -> bool:
+    """Whether fp16 operands pay for their staging on this shape: they take
+    about 8 % off the GEMM kernel's time, and the staging kernel costs about
+    4.5 us plus its 4 bytes per activation at ~5 TB/s (MI355X, measured at
+    M = 512, K = 5120: a loss at N = 14336, a gain at N = 17408 and above).
+    The results are the same either way."""
+    t_gemm = 2.0 * M * N * K / 1.0e15
+    t_stage = 4.5e-6 + 4.0 * M * K / 5.0e12
+    return 0.08 * t_gemm > t_stage
+
+
 def _gemm_workspace(dev, workspace, M, N, K, stream):
     """The workspace a GEMM call passes: workspace=None takes the per-stream
-    scratch (fp16 operands), workspace=False none (bf16 operands)."""
+    scratch (fp16 operands) where gemm_staging_pays, else none; False none
+    (bf16 operands); a tensor is passed as given."""
     if workspace is None:
+        if not gemm_staging_pays(M, N, K):
+            return None
         return gemm_scratch(dev, q4proj_gemm_workspace_bytes(M, N, K), stream)
     if workspace is False:
         return None
@@ -366,9 +380,10 @@ def q4proj_gemv_noalloc(packed_codes, packed_scales, global_scale: float, x, y, 
 def q4proj_gemm(packed_codes, packed_scales, global_scale: float, x, y, M: int, N: int, K: int,
                 workspace=None, stream=None) -> None:
     """y[M][N] fp32 = x[M][K] bf16 . dequant(W)^T for any M >= 1.
-    workspace: None takes the stream's GEMM scratch (fp16 operands), False
-    runs without one (bf16 operands, the same results), or a uint8 tensor of
-    q4proj_gemm_workspace_bytes(M, N, K) bytes."""
+    workspace: None takes the stream's GEMM scratch (fp16 operands) on shapes
+    where that pays (gemm_staging_pays) and none otherwise, False runs
+    without one (bf16 operands, the same results), a uint8 tensor of
+    q4proj_gemm_workspace_bytes(M, N, K) bytes is used as given."""
     _proj(_lib.q4proj_gemm, "q4proj_gemm", packed_codes, packed_scales, global_scale, x, y, M, N,
           K, workspace, stream)
 

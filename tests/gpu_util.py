@@ -43,12 +43,19 @@ def project(kind: str, packed, g: float, x: np.ndarray, N: int, K: int) -> np.nd
     if kind == "gemv":
         m.q4proj_gemv(packed[0], packed[1], g, xd, y, M, N, K)
     else:
-        # "gemm": fp16 operands (the binding's GEMM scratch); "gemm_bf16": no
-        # workspace, bf16 operands
-        m.q4proj_gemm(packed[0], packed[1], g, xd, y, M, N, K,
-                      workspace=False if kind == "gemm_bf16" else None)
+        # "gemm": fp16 operands (an explicit staging workspace, whatever the
+        # shape); "gemm_bf16": no workspace, bf16 operands
+        ws = False if kind == "gemm_bf16" else gemm_workspace(M, N, K)
+        m.q4proj_gemm(packed[0], packed[1], g, xd, y, M, N, K, workspace=ws)
     torch.cuda.synchronize()
     return y.cpu().numpy()
+
+
+def gemm_workspace(M: int, N: int, K: int) -> torch.Tensor:
+    """A staging workspace for the GEMMs (fp16 operands), filled with a
+    pattern: it needs no contents."""
+    return torch.full((q4().q4proj_gemm_workspace_bytes(M, N, K),), 0xA5, dtype=torch.uint8,
+                      device=DEV)
 
 
 def run(kind: str, codes, scales, g, x) -> np.ndarray:

@@ -181,6 +181,19 @@ def test_gemm_workspace_validation(q4):
     assert q4.q4proj_gemm_workspace_bytes(1, 64, 250) == 0
 
 
+def test_binding_stages_gemm_activations_where_it_pays(q4):
+    # the binding's default GEMM call stages fp16 operands only where its
+    # estimate says the kernel time saved exceeds the staging: at M = 512,
+    # K = 5120 not for the qkv width, for gate/up and the fused pair; not at
+    # small M, nor for the 17408-wide rows of the down projection at M = 512
+    assert not q4.gemm_staging_pays(512, 14336, 5120)
+    assert q4.gemm_staging_pays(512, 17408, 5120)
+    assert q4.gemm_staging_pays(512, 34816, 5120)
+    assert not q4.gemm_staging_pays(64, 17408, 5120)
+    assert not q4.gemm_staging_pays(512, 5120, 17408)
+    assert q4.gemm_staging_pays(4096, 14336, 5120)
+
+
 def test_gemv_m_range(q4):
     lib = q4.library()
     assert proj(lib, "q4proj_gemv", M=17) == q4.EUNSUPPORTED

@@ -23,7 +23,7 @@ import torch
 
 import oracle
 import synth
-from gpu_util import DEV, assert_parity, bits, note, pack, q4, to_dev_x
+from gpu_util import DEV, assert_parity, bits, gemm_workspace, note, pack, q4, to_dev_x
 
 pytestmark = pytest.mark.gpu
 
@@ -164,14 +164,15 @@ def test_fp16_and_bf16_paths_agree_bitwise(M, N, K):
     x = synth.x_bf16(80 + M, 4, M, K)
     packed = pack(w.codes, w.scales, N, K)
     note(f"gemm fp16/bf16 M={M} N={N} K={K}")
-    y16 = run_gemm(packed, w.g, x, N, K, None)
+    ws = gemm_workspace(M, N, K)
+    y16 = run_gemm(packed, w.g, x, N, K, ws)
     y32 = run_gemm(packed, w.g, x, N, K, False)
     assert np.array_equal(bits(y16), bits(y32))
     assert_parity(w.codes, w.scales, w.g, x, y16)
     if N % 16 == 0:
         F = N // 2
         note(f"gemm_silu_mul fp16/bf16 M={M} F={F} K={K}")
-        assert np.array_equal(run_silu(packed, w.g, x, F, K, None),
+        assert np.array_equal(run_silu(packed, w.g, x, F, K, ws),
                               run_silu(packed, w.g, x, F, K, False))
 
 
@@ -186,16 +187,17 @@ def test_full_size_prefill_paths_agree(N, silu):
     x = synth.x_bf16(90, 2, M, K)
     packed = pack(w.codes, w.scales, N, K)
     xd = to_dev_x(x)
+    wsp = gemm_workspace(M, N, K)
     if silu:
         F = N // 2
         outs = [torch.full((M, F), -1, dtype=torch.int16, device=DEV) for _ in range(2)]
-        for o, ws in zip(outs, (None, False)):
-            note(f"gemm_silu_mul M={M} F={F} K={K} workspace={ws}")
+        for o, ws in zip(outs, (wsp, False)):
+            note(f"gemm_silu_mul M={M} F={F} K={K} staged={ws is not False}")
             m.q4proj_gemm_silu_mul(packed[0], packed[1], w.g, xd, o, M, F, K, workspace=ws)
     else:
         outs = [torch.full((M, N), float("nan"), dtype=torch.float32, device=DEV) for _ in range(2)]
-        for o, ws in zip(outs, (None, False)):
-            note(f"gemm M={M} N={N} K={K} workspace={ws}")
+        for o, ws in zip(outs, (wsp, False)):
+            note(f"gemm M={M} N={N} K={K} staged={ws is not False}")
             m.q4proj_gemm(packed[0], packed[1], w.g, xd, o, M, N, K, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(outs[0], outs[1])
@@ -226,3 +228,4 @@ def test_workspace_reused_across_sizes():
         y32 = run_gemm(packed, w.g, x, N, K, False)
         assert np.array_equal(bits(y16), bits(y32))
         assert_parity(w.codes, w.scales, w.g, x, y16)
+
