@@ -1,8 +1,9 @@
 /*
  * A plain C consumer of the q4proj C ABI (include/q4proj.h): no Python, no
  * torch.  It allocates device memory with the HIP runtime, packs a seeded
- * NVFP4 weight, runs q4proj_gemv (M = 3) and q4proj_gemm (M = 40) on a
- * stream of its own, unpacks the weight again, and checks every output
+ * NVFP4 weight, runs q4proj_gemv (M = 3) and q4proj_gemm (M = 40, without
+ * and with its fp16 staging workspace, bit for bit alike) on a stream of its
+ * own, unpacks the weight again, and checks every output
  * against the CPU oracle (oracle/oracle.c, fp64) with the projection's
  * tolerance |y - y_ref| <= 2e-3 * sum_k |x_k w_k|.  It then builds a fused
  * gate/up weight from two separate weights (q4proj_pack_gate_up) and runs
@@ -112,12 +113,26 @@ int abi_consumer_run(void)
     CHECK(q4proj_status_string(Q4P_EHIP) != NULL, "status string");
 
     CHECK(orc_proj(MG, N, K, codes, scales, (double)g, x, yref, S, 4) == 0, "oracle");
-    const struct { const char *name; int64_t M; } runs[2] = {{"q4proj_gemv", MV}, {"q4proj_gemm", MG}};
-    for (int i = 0; i < 2; ++i) {
+    /* the GEMMs' optional staging workspace: fp16 operands, the same results */
+    const size_t gwsb = q4proj_gemm_workspace_bytes(MG, N, K);
+    CHECK(gwsb == (size_t)(MG * K * 2 + 255) / 256 * 256 + (size_t)(MG * 4 + 255) / 256 * 256,
+          "gemm workspace size %zu", gwsb);
+    void *d_gws = dev_alloc(gwsb);
+    CHECK(d_gws != NULL, "device allocation (gemm workspace)");
+    st = q4proj_gemm(d_pc, d_ps, g, d_x, d_y, MG, N, K, d_gws, gwsb - 1, stream);
+    CHECK(st == Q4P_EWORKSPACE, "gemm short workspace gave %d", (int)st);
+    st = q4proj_gemm(d_pc, d_ps, g, d_x, d_y, MG, N, K, d_x, gwsb, stream);
+    CHECK(st == Q4P_EINVAL, "gemm workspace overlapping x gave %d", (int)st);
+    float *ybf = malloc((size_t)(MG * N) * 4);
+    CHECK(ybf != NULL, "host allocation");
+    const struct { const char *name; int64_t M; } runs[3] = {
+        {"q4proj_gemv", MV}, {"q4proj_gemm", MG}, {"q4proj_gemm (staged fp16)", MG}};
+    for (int i = 0; i < 3; ++i) {
         const int64_t M = runs[i].M;
         HIP(hipMemsetAsync(d_y, 0xFF, (size_t)(M * N) * 4, stream));    /* NaN fill */
-        st = i == 0 ? q4proj_gemv(d_pc, d_ps, g, d_x, d_y, M, N, K, d_ws, wsb, stream)
-                    : q4proj_gemm(d_pc, d_ps, g, d_x, d_y, M, N, K, NULL, 0, stream);
+        st = i == 0   ? q4proj_gemv(d_pc, d_ps, g, d_x, d_y, M, N, K, d_ws, wsb, stream)
+             : i == 1 ? q4proj_gemm(d_pc, d_ps, g, d_x, d_y, M, N, K, NULL, 0, stream)
+                      : q4proj_gemm(d_pc, d_ps, g, d_x, d_y, M, N, K, d_gws, gwsb, stream);
         CHECK(st == Q4P_OK, "%s: %s", runs[i].name, q4proj_status_string(st));
         HIP(hipStreamSynchronize(stream));
         HIP(hipMemcpy(y, d_y, (size_t)(M * N) * 4, hipMemcpyDeviceToHost));
@@ -128,7 +143,13 @@ int abi_consumer_run(void)
               (long long)bad, (long long)(M * N));
         printf("%s M=%lld N=%lld K=%lld ok, max |y-y_ref|/S = %.3g\n", runs[i].name,
                (long long)M, (long long)N, (long long)K, worst);
+        if (i == 1)
+            memcpy(ybf, y, (size_t)(M * N) * 4);
+        if (i == 2)
+            CHECK(memcmp(ybf, y, (size_t)(M * N) * 4) == 0, "staged gemm differs from bf16 gemm");
     }
+    free(ybf);
+    hipFree(d_gws);
 
     st = q4proj_unpack(d_pc, d_ps, N, K, d_codes, d_scales, stream);
     CHECK(st == Q4P_OK, "q4proj_unpack: %s", q4proj_status_string(st));
