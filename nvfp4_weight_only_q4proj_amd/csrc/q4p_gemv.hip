@@ -412,6 +412,11 @@ gemv_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
 constexpr int kSkMaxGroups = 256;
 constexpr int kSkMaxWaves = 8;
 constexpr int kSkPrefetch = 4;
+// ring depth for M <= 4 with one K range when a wave streams few units (the
+// 4B-model decode shapes, ~6 units per wave): three in flight were 1-2.5 %
+// faster there, and slower on the 50 MB shapes (21 units per wave)
+constexpr int kSkPrefetchShort = 3;
+constexpr int kSkShortUnits = 10;
 // activations of a range in LDS: all of a CU's 160 KB beside the zero strip
 // and the partial sums of 8 waves (2 x 1 KB each)
 constexpr int kSkXMaxBytes = 160 * 1024 - kZeroBytes - kSkMaxWaves * 2 * 64 * 16;
@@ -1139,17 +1144,20 @@ gemv_sk_fn pick_sk_kernel_k(int64_t M)
 }
 
 template <int EPI>
-gemv_sk_fn pick_sk_kernel_e(int64_t M, bool ranges)
+gemv_sk_fn pick_sk_kernel_e(int64_t M, bool ranges, bool short_waves)
 {
+    if (!ranges && M <= 4 && short_waves)
+        return gemv_sk_kernel<1, kSkPrefetchShort, false, EPI>;
     return ranges ? pick_sk_kernel_k<true, EPI>(M) : pick_sk_kernel_k<false, EPI>(M);
 }
 
-gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges, int epi)
+// short_waves: every wave streams at most kSkShortUnits units
+gemv_sk_fn pick_sk_kernel(int64_t M, bool ranges, int epi, bool short_waves)
 {
     switch (epi) {
-    case kEpiSilu: return pick_sk_kernel_e<kEpiSilu>(M, ranges);
-    case kEpiArgmax: return pick_sk_kernel_e<kEpiArgmax>(M, ranges);
-    default: return pick_sk_kernel_e<kEpiY>(M, ranges);
+    case kEpiSilu: return pick_sk_kernel_e<kEpiSilu>(M, ranges, short_waves);
+    case kEpiArgmax: return pick_sk_kernel_e<kEpiArgmax>(M, ranges, short_waves);
+    default: return pick_sk_kernel_e<kEpiY>(M, ranges, short_waves);
     }
 }
 
@@ -1240,7 +1248,10 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, int epi)
     if (WPG > ULAST / GR)
         WPG = ULAST / GR;
     SkPlan p;
-    p.fn = pick_sk_kernel(M, KS > 1, epi);
+    // units of the busiest wave: ceil(ceil(units of the range / GR) / WPG)
+    const int64_t UR = NT * KTR;
+    const int64_t wave_units = ((UR + GR - 1) / GR + WPG - 1) / WPG;
+    p.fn = pick_sk_kernel(M, KS > 1, epi, wave_units <= kSkShortUnits);
     p.args = SkArgs{(int)M, (int)N, (int)K, (int)KT, (int)NT, (int)(GR * KS), (int)WPG, (int)KS,
                     (int)KTR, 0.f, nullptr, nullptr};
     size_t lds = (size_t)(M * KTR * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
