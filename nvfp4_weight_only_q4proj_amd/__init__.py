@@ -294,11 +294,11 @@ def gemm_scratch(device, nbytes: int, stream=None):
 def gemm_staging_pays(M: int, N: int, K: int) -> bool:
     """Whether fp16 operands pay for their staging on this shape: they take
     about 8 % off the GEMM kernel's time, and the staging kernel costs about
-    4.5 us plus its 4 bytes per activation at ~5 TB/s (MI355X, measured at
-    M = 512, K = 5120: a loss at N = 14336, a gain at N = 17408 and above).
+    4 us plus its 4 bytes per activation at ~5 TB/s (MI355X, measured at
+    M = 512, K = 5120: level at N = 14336, a gain at N = 17408 and above).
     The results are the same either way."""
     t_gemm = 2.0 * M * N * K / 1.0e15
-    t_stage = 4.5e-6 + 4.0 * M * K / 5.0e12
+    t_stage = 4.0e-6 + 4.0 * M * K / 5.0e12
     return 0.08 * t_gemm > t_stage
 
 

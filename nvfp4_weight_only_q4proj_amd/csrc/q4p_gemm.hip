@@ -647,7 +647,7 @@ gemm_kernel(const uint8_t *__restrict__ pcodes, const uint8_t *__restrict__ psca
 // exactly; it is NaN when the row would not convert exactly, holds an
 // infinity or a NaN, or g * 2^c is not a normal float (or g is not finite),
 // and the GEMM then runs the bf16 loop for that row's block.
-// One wave per row (four rows per 256-thread workgroup); K % 8 == 0.
+// One 256-thread workgroup (four waves) per row; K % 8 == 0.
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 // floor(log2 v) of the nonzero finite bf16 magnitude with bit pattern a
@@ -657,19 +657,39 @@ __device__ __forceinline__ int bf16_exponent(uint32_t a)
     return e ? (int)e - 127 : (31 - __builtin_clz(a & 0x7fu)) - 133;
 }
 
+// max (MAX) or min over each 16-lane row of the wave by DPP butterflies
+// (lane ^ 1, lane ^ 2, then the half-row and row mirrors), then over the
+// four rows by readlane: a wave-uniform result
+template <bool MAX>
+__device__ __forceinline__ uint32_t wave_reduce_u32(uint32_t v)
+{
+    auto step = [&](uint32_t t) { v = MAX ? (t > v ? t : v) : (t < v ? t : v); };
+    step((uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false));    // quad_perm 1,0,3,2
+    step((uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false));    // quad_perm 2,3,0,1
+    step((uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x141, 0xF, 0xF, false));   // row_half_mirror
+    step((uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x140, 0xF, 0xF, false));   // row_mirror
+    uint32_t r = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+#pragma unroll
+    for (int l = 16; l < 64; l += 16) {
+        const uint32_t t = (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+        r = MAX ? (t > r ? t : r) : (t < r ? t : r);
+    }
+    return r;
+}
+
 __global__ void __launch_bounds__(256)
 gemm_xprep_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K, float g,
                   uint16_t *__restrict__ xh, float *__restrict__ rowmul)
 {
-    // 16-byte chunks (8 values) of the row: lane l takes chunks l, l + 64,
+    // 16-byte chunks (8 values) of the row: thread t takes chunks t, t + 256,
     // ...; the first kHeld of them stay in registers between the two passes
     // (rows up to K = 8192), the rest are read again.  Buffer accesses past
     // the row read zero / are dropped.
-    constexpr int kHeld = 16;
-    const int64_t m = (int64_t)blockIdx.x * 4 + __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-    if (m >= M)
-        return;
-    const uint32_t lane = threadIdx.x & 63;
+    constexpr int kHeld = 4;
+    __shared__ uint32_t part[8];
+    const int64_t m = blockIdx.x;
+    const uint32_t t = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane((int)(t >> 6));
     const uint32_t row_bytes = (uint32_t)(K * 2);
     const __amdgpu_buffer_rsrc_t xs = make_rsrc(x + m * K, row_bytes);
     const __amdgpu_buffer_rsrc_t hs = make_rsrc(xh + m * K, row_bytes);
@@ -692,20 +712,25 @@ gemm_xprep_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K, float g,
     u32x4_t held[kHeld];
 #pragma unroll
     for (int i = 0; i < kHeld; ++i)
-        held[i] = load(lane + 64u * i);
+        held[i] = load(t + 256u * i);
 #pragma unroll
     for (int i = 0; i < kHeld; ++i)
         scan(held[i]);
-    for (uint32_t ch = lane + 64u * kHeld; ch < nchunks; ch += 64u)
+    for (uint32_t ch = t + 256u * kHeld; ch < nchunks; ch += 256u)
         scan(load(ch));
-    uint32_t hi_bits = amax[0] > amax[1] ? amax[0] : amax[1];
-    uint32_t lo_bits1 = amin1[0] < amin1[1] ? amin1[0] : amin1[1];
+    // the four waves' results through LDS
+    const uint32_t wmax = wave_reduce_u32<true>(amax[0] > amax[1] ? amax[0] : amax[1]);
+    const uint32_t wmin = wave_reduce_u32<false>(amin1[0] < amin1[1] ? amin1[0] : amin1[1]);
+    if ((t & 63) == 0) {
+        part[wave] = wmax;
+        part[4 + wave] = wmin;
+    }
+    __syncthreads();
+    uint32_t hi_bits = part[0], lo_bits1 = part[4];
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-        const uint32_t h2 = (uint32_t)__shfl_xor((int)hi_bits, off, 64);
-        const uint32_t l2 = (uint32_t)__shfl_xor((int)lo_bits1, off, 64);
-        hi_bits = h2 > hi_bits ? h2 : hi_bits;
-        lo_bits1 = l2 < lo_bits1 ? l2 : lo_bits1;
+    for (int w = 1; w < 4; ++w) {
+        hi_bits = part[w] > hi_bits ? part[w] : hi_bits;
+        lo_bits1 = part[4 + w] < lo_bits1 ? part[4 + w] : lo_bits1;
     }
     const bool nonfinite = hi_bits >= 0x7f80u;
     const bool zero_row = hi_bits == 0;
@@ -726,11 +751,11 @@ gemm_xprep_kernel(const uint16_t *__restrict__ x, int64_t M, int64_t K, float g,
     if (exact) {
 #pragma unroll
         for (int i = 0; i < kHeld; ++i)
-            convert_store(held[i], lane + 64u * i);
-        for (uint32_t ch = lane + 64u * kHeld; ch < nchunks; ch += 64u)
+            convert_store(held[i], t + 256u * i);
+        for (uint32_t ch = t + 256u * kHeld; ch < nchunks; ch += 256u)
             convert_store(load(ch), ch);
     }
-    if (lane == 0) {
+    if (t == 0) {
         const float gm = __builtin_ldexpf(g, c);
         const float agm = __builtin_fabsf(gm);
         const bool mul_ok = g == 0.0f || (agm >= 1.17549435e-38f && agm <= 3.40282347e+38f);
@@ -777,7 +802,7 @@ hipError_t launch_gemm_any(const uint8_t *packed_codes, const uint8_t *packed_sc
     if (workspace) {
         xh = static_cast<uint16_t *>(workspace);
         rowmul = reinterpret_cast<float *>(static_cast<uint8_t *>(workspace) + align256(M * K * 2));
-        hipLaunchKernelGGL(gemm_xprep_kernel, dim3((unsigned)((M + 3) / 4)), dim3(256), 0, stream, x,
+        hipLaunchKernelGGL(gemm_xprep_kernel, dim3((unsigned)M), dim3(256), 0, stream, x,
                            M, K, g, xh, rowmul);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess)
