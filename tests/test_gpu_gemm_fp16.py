@@ -15,6 +15,8 @@ in the same order, so their outputs must agree bit for bit.
 * fp16 and bf16 paths bitwise equal on those rows (NaN positions equal), on
   ragged shapes and on the full M = 512 prefill shapes, plain and fused;
 * every finite row within the oracle's tolerance;
+* rows longer than the 8192 values the staging kernel keeps in registers,
+  with their extremes, an infinity and a NaN past that point;
 * one workspace reused by calls of different sizes, no contents required.
 """
 import numpy as np
@@ -157,7 +159,47 @@ def test_staging_and_paths_on_special_rows():
     assert np.array_equal(nan16, nan32) and np.array_equal(h16[~nan16], h32[~nan32])
 
 
-@pytest.mark.parametrize("M,N,K", [(129, 300, 1040), (513, 100, 272), (1, 17, 5136),
+def test_staging_long_rows():
+    """Rows longer than the 8192 values the staging kernel holds in
+    registers: the chunks past them are scanned and converted on a second
+    read, so the row's extremes are placed there."""
+    m = q4()
+    M, N, K = 136, 64, 12304
+    w = synth.nvfp4_normal_matrix(91, 1, N, K)
+    x = synth.x_bf16(91, 9, M, K)
+    x[1, 12000] = bf16(2.0 ** 12)                # the row's largest value, past 8192
+    # row 2: magnitudes capped at 0.5 (largest exponent -1) and one 2^-30
+    # past 8192: 29 binades, exact at the boundary
+    x[2] = np.where(np.abs((x[2].astype(np.uint32) << 16).view(np.float32)) > 0.5,
+                    bf16(0.25), x[2]).astype(np.uint16)
+    x[2, 10] = bf16(0.5)
+    x[2, 9000] = bf16(2.0 ** -30)
+    x[130] = 0                                   # 30 binades, the small end past 8192
+    x[130, 5], x[130, 10000] = bf16(2.0 ** 20), bf16(2.0 ** -10)
+    x[131, 11000] = 0x7F80                       # +Inf past 8192
+    x[132, K - 1] = 0xFFC0                       # NaN in the last chunk
+    packed = pack(w.codes, w.scales, N, K)
+    need = m.q4proj_gemm_workspace_bytes(M, N, K)
+    ws = torch.full((need,), 0x55, dtype=torch.uint8, device=DEV)
+    note(f"gemm fp16 staging, long rows M={M} N={N} K={K}")
+    y16 = run_gemm(packed, w.g, x, N, K, ws)
+    wsh = ws.cpu().numpy()
+    xh = wsh[:2 * M * K].view(np.float16).reshape(M, K)
+    rowmul = wsh[r256(2 * M * K):r256(2 * M * K) + 4 * M].view(np.float32)
+    xh_ref, rowmul_ref = staging_model(x, w.g)
+    assert list(np.flatnonzero(np.isnan(rowmul_ref))) == [130, 131, 132]
+    assert np.array_equal(np.isnan(rowmul), np.isnan(rowmul_ref))
+    ok = ~np.isnan(rowmul_ref)
+    assert np.array_equal(rowmul[ok].view(np.uint32), rowmul_ref[ok].view(np.uint32))
+    for r in np.flatnonzero(ok):
+        assert np.array_equal(xh[r].view(np.uint16), xh_ref[r].view(np.uint16)), r
+    note("gemm bf16 path on the same rows")
+    y32 = run_gemm(packed, w.g, x, N, K, False)
+    assert same_bits_nan_aware(y16, y32)
+    assert_parity(w.codes, w.scales, w.g, x, y16, xrows=np.arange(128))
+
+
+@pytest.mark.parametrize("M,N,K", [(129, 300, 1040), (513, 100, 272), (1, 17, 5136), (3, 40, 16),
                                    (200, 4112, 128), (64, 2049, 400), (300, 48, 2000)])
 def test_fp16_and_bf16_paths_agree_bitwise(M, N, K):
     w = synth.nvfp4_normal_matrix(80 + M, 3, N, K)
