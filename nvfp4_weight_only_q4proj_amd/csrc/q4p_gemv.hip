@@ -436,6 +436,15 @@ struct SkArgs {
     float g;
     float *best_val;                           // argmax epilogue: per-row result
     int64_t *best_idx;
+    // Division-free set-up, filled by the host: workgroups per K range; per
+    // range kind (0: KTR k-tiles, 1: the shorter last range) the units per
+    // workgroup (base, remainder) and the per-wave split (base, remainder)
+    // of a workgroup range of `base` and of `base + 1` units; and
+    // ceil(2^32 / (16 * k-tiles)), so that umulhi(i, xrcp) = i / (16 * k-tiles)
+    // for the staging group indices i (i * 16 * k-tiles < 2^32).
+    int GR;
+    int split[2][6];
+    uint32_t xrcp[2];
 };
 
 // Epilogues of the stream-K kernel
@@ -545,25 +554,25 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int LG = blockIdx.x;
     // K range of this workgroup: k-tiles c0 .. c0 + KT - 1, streamed by the
     // GR workgroups of that range; below, units, KT and L are range-local
-    const int GR = G / a.KS;
-    const int kr = LG / GR;
+    // (Every instruction before the first loads, and after the stream, adds
+    // to the launch: the divisions of this set-up come from the host.)
+    const int GR = a.GR;
+    const int kr = KR ? LG / GR : 0;
     const int L = LG - kr * GR;
     const int c0 = kr * a.KTR;
     const int KT = KTG - c0 < a.KTR ? KTG - c0 : a.KTR;
-    const int U = a.NT * KT;
-    const int ubase = U / GR, urem = U - ubase * GR;
+    const int kind = KR && KT != a.KTR ? 1 : 0;
     // balanced split: the first `urem` groups (and, inside a group, the first
     // `wr` waves) take one unit more
-    const int UW0 = L * ubase + (L < urem ? L : urem);
-    const int UWn = ubase + (L < urem ? 1 : 0);
+    const int ubase = kind ? a.split[1][0] : a.split[0][0];
+    const int urem = kind ? a.split[1][1] : a.split[0][1];
+    const bool more = L < urem;
+    const int UW0 = L * ubase + (more ? L : urem);
+    const int UWn = ubase + (more ? 1 : 0);
     const int UW1 = UW0 + UWn;
-    const int wb = UWn / WPG, wr = UWn - wb * WPG;
+    const int wb = kind ? (more ? a.split[1][4] : a.split[1][2]) : (more ? a.split[0][4] : a.split[0][2]);
+    const int wr = kind ? (more ? a.split[1][5] : a.split[1][3]) : (more ? a.split[0][5] : a.split[0][3]);
     auto wave_start = [&](int v) { return UW0 + v * wb + (v < wr ? v : wr); };
-    // wave of this workgroup that holds unit u (UW0 <= u < UW1)
-    auto wave_of = [&](int u) {
-        const int o = u - UW0, big = wr * (wb + 1);
-        return o < big ? o / (wb + 1) : wr + (o - big) / wb;
-    };
     const int u0 = wave_start(wave), u1 = wave_start(wave + 1);
     const int n = u1 - u0;
     const int ulast = n > 0 ? u1 - 1 : 0;
@@ -579,21 +588,18 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     const int gpr = KT * 16;                   // 16-byte groups per activation row
     const int kbase = c0 * 128;
     const int ngroups = M * gpr;
-    // group tid + i*nthr is (row srow[i], group sq[i] of that row): walk the
-    // rows instead of dividing
+    // group tid + i*nthr is (row srow[i], group sq[i] of that row); rows past
+    // M are marked M
     uint4 xs[kSkStage];
     int srow[kSkStage], sq[kSkStage];
     {
-        int row = 0, q = (int)threadIdx.x;
+        const uint32_t xrcp = kind ? a.xrcp[1] : a.xrcp[0];
 #pragma unroll
         for (int i = 0; i < kSkStage; ++i) {
-            while (q >= gpr && row < M) {
-                q -= gpr;
-                ++row;
-            }
-            srow[i] = row;
-            sq[i] = q;
-            q += nthr;
+            const uint32_t gi = threadIdx.x + (uint32_t)(i * nthr);
+            const int row = (int)__umulhi(gi, xrcp);
+            srow[i] = row < M ? row : M;
+            sq[i] = (int)gi - row * gpr;
         }
     }
 #pragma unroll
@@ -895,26 +901,26 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
 
     // 5. finish the row tiles split between waves or workgroups
     __syncthreads();
-    const int tlast = n > 0 ? (u1 - 1) / KT : 0;
+    // the stream leaves t one past the wave's last row tile, or on it when
+    // (K ranges) that tile's last unit was not this wave's
+    const int tlast = n == 0 ? 0 : KR && c != 0 ? t : t - 1;
     for (int side = 0; side < (n > 0 ? 2 : 0); ++side) {
         const int tau = side == 0 ? tfirst : tlast;
         if (side == 1 && tlast == tfirst)
             break;
         const int ta = tau * KT, tb = ta + KT;
         const int a0 = ta > UW0 ? ta : UW0, a1 = tb < UW1 ? tb : UW1;
-        const int vlo = wave_of(a0), vhi = wave_of(a1 - 1);
         const bool cross = ta < UW0 || tb > UW1;
-        if (vlo != wave || (vlo == vhi && !cross))
-            continue;                                   // another wave's, or stored already
-        floatx4_t sum = {0.f, 0.f, 0.f, 0.f};
-        for (int v = vlo; v <= vhi; ++v) {
-            const int vfirst = wave_start(v) / KT;
-            const floatx4_t pv = part[(v * 2 + (tau == vfirst ? 0 : 1)) * 64 + lane];
-            if (v == vlo)
-                sum = pv;
-            else
-                sum += pv;
-        }
+        // this wave holds the tile's first units in the workgroup when the
+        // tile starts inside its range, and all of them when the tile also
+        // ends inside it (stored already, unless it crosses into a neighbour)
+        if (a0 < u0 || (a1 <= u1 && !cross))
+            continue;
+        // the later waves whose ranges start inside the tile hold the rest,
+        // each as the partial of its first tile; summed in wave order
+        floatx4_t sum = part[(wave * 2 + side) * 64 + lane];
+        for (int v = wave + 1; v < WPG && wave_start(v) < a1; ++v)
+            sum += part[v * 2 * 64 + lane];
         if (!cross) {
             store_y(tau, sum);
             continue;
@@ -1254,6 +1260,26 @@ SkPlan make_sk_plan(int64_t M, int64_t N, int64_t K, int epi)
     p.fn = pick_sk_kernel(M, KS > 1, epi, wave_units <= kSkShortUnits);
     p.args = SkArgs{(int)M, (int)N, (int)K, (int)KT, (int)NT, (int)(GR * KS), (int)WPG, (int)KS,
                     (int)KTR, 0.f, nullptr, nullptr};
+    p.args.GR = (int)GR;
+    for (int kind = 0; kind < 2; ++kind) {
+        // sk_ranges leaves no range without k-tiles: the last has 1..KTR
+        const int64_t KTx = kind == 0 ? KTR : KT - (KS - 1) * KTR;
+        const int64_t U = NT * KTx, ub = U / GR;
+        int *sp = p.args.split[kind];
+        sp[0] = (int)ub;
+        sp[1] = (int)(U % GR);
+        sp[2] = (int)(ub / WPG);
+        sp[3] = (int)(ub % WPG);
+        sp[4] = (int)((ub + 1) / WPG);
+        sp[5] = (int)((ub + 1) % WPG);
+        // exact for every staging group index i: umulhi(i, ceil(2^32 / d))
+        // is i / d while i * d < 2^32, and i < 16 slots * 512 threads while
+        // d = 16 * KTx is bounded by the range's activations fitting in LDS
+        static_assert((uint64_t)16 * 64 * kSkMaxWaves * 16 * (kSkXMaxBytes / 256) < (uint64_t(1) << 32),
+                      "staging reciprocal out of its exact range");
+        const uint64_t gpr = 16 * (uint64_t)KTx;
+        p.args.xrcp[kind] = (uint32_t)(((uint64_t(1) << 32) + gpr - 1) / gpr);
+    }
     size_t lds = (size_t)(M * KTR * 256) + kZeroBytes + (size_t)WPG * 2 * 64 * sizeof(floatx4_t);
     if (lds < (size_t)kSkLdsFloor)
         lds = kSkLdsFloor;
