@@ -408,6 +408,11 @@ gemv_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscales,
 // completes one row completes its partner row too.  KS trades staging (every
 // workgroup reads its range's activations into LDS) against joining; the
 // launcher picks the count with the least measured cost (sk_ranges).
+//
+// Every wave starts at once and the launch ends with the last finish, so the
+// scalar work before a wave's first loads and after its last unit adds to
+// every launch: the host precomputes the unit split and a reciprocal for
+// the staging map, and the finish finds its partner waves without dividing.
 
 constexpr int kSkMaxGroups = 256;
 constexpr int kSkMaxWaves = 8;
