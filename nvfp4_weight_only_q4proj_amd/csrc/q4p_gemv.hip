@@ -558,9 +558,9 @@ gemv_sk_kernel(const uint4 *__restrict__ pcodes, const uint2 *__restrict__ pscal
     // better.)
     const int LG = blockIdx.x;
     // K range of this workgroup: k-tiles c0 .. c0 + KT - 1, streamed by the
-    // GR workgroups of that range; below, units, KT and L are range-local
-    // (Every instruction before the first loads, and after the stream, adds
-    // to the launch: the divisions of this set-up come from the host.)
+    // GR workgroups of that range; below, units, KT and L are range-local.
+    // Every instruction before the first loads adds to the launch, so the
+    // divisions of this set-up come precomputed from the host (a.split).
     const int GR = a.GR;
     const int kr = KR ? LG / GR : 0;
     const int L = LG - kr * GR;
